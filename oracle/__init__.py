@@ -1,0 +1,182 @@
+"""fp64 CPU attention oracle -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never calls it, and it
+imports nothing from the GPU package: the two share only the seeded input
+generators (``attn_inputs``), which hold none of the method's arithmetic.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, OpenMP over rows); this
+module builds it with gcc and marshals arrays.  Every function takes tensors or
+arrays of any float dtype (bf16 widens to fp64 exactly) and returns float64
+numpy arrays.
+
+What it computes is the plain definition of softmax attention (scores, stable
+softmax, weighted sum of values, L = m + ln l) and its exact gradient; the
+sources on the FlashAttention pages are cited in ``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I64 = ctypes.POINTER(ctypes.c_int64)
+_I32 = ctypes.POINTER(ctypes.c_int32)
+_i64 = ctypes.c_int64
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.run(
+            ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+             "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"],
+            check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or (
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_attn_fwd.argtypes = [_D, _D, _D, _D, _D, _i64, _i64, _i64,
+                                    _i64, ctypes.c_double, ctypes.c_int]
+    lib.oracle_attn_fwd_rows.argtypes = [_D, _D, _D, _I64, _I64, _i64, _D, _D,
+                                         _i64, _i64, _i64, _i64,
+                                         ctypes.c_double, ctypes.c_int]
+    lib.oracle_attn_fwd_varlen.argtypes = [_D, _D, _D, _D, _D, _I32, _i64,
+                                           _i64, _i64, _i64, ctypes.c_double,
+                                           ctypes.c_int]
+    lib.oracle_attn_fwd_varlen_rows.argtypes = [
+        _D, _D, _D, _I32, _i64, _i64, _i64, _i64, ctypes.c_double,
+        ctypes.c_int, _I64, _I64, _i64, _D, _D]
+    lib.oracle_attn_bwd.argtypes = [_D, _D, _D, _D, _D, _D, _D, _i64, _i64,
+                                    _i64, _i64, ctypes.c_double, ctypes.c_int]
+    for f in (lib.oracle_attn_fwd, lib.oracle_attn_fwd_rows,
+              lib.oracle_attn_fwd_varlen, lib.oracle_attn_fwd_varlen_rows,
+              lib.oracle_attn_bwd):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use (OMP_NUM_THREADS or all cores)."""
+    return int(_load().oracle_num_threads())
+
+
+def _f64(x) -> np.ndarray:
+    """Any tensor/array -> C-contiguous float64 numpy (bf16 widens exactly)."""
+    if hasattr(x, "detach"):  # torch tensor, possibly on a GPU
+        import torch
+        x = x.detach().to(device="cpu", dtype=torch.float64).contiguous().numpy()
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _p(a: np.ndarray, t=_D):
+    return a.ctypes.data_as(t)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise RuntimeError("oracle %s failed with code %d" % (what, rc))
+
+
+def fwd(q, k, v, scale: float, causal: bool):
+    """Dense forward.  q, k, v: [B, H, N, D].  Returns (O [B,H,N,D], L [B,H,N])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, D = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    o = np.empty_like(q)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    _check(_load().oracle_attn_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H,
+                                   N, D, float(scale), int(bool(causal))),
+           "fwd")
+    return o, lse
+
+
+def fwd_rows(q, k, v, scale: float, causal: bool, bh, rows):
+    """Selected rows of the dense forward.
+
+    bh[t] is the flattened head index b*H + h, rows[t] the query row.
+    Returns (O_rows [n, D], L_rows [n]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, D = q.shape
+    bh = np.ascontiguousarray(bh, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    n = bh.shape[0]
+    o = np.empty((n, D), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    _check(_load().oracle_attn_fwd_rows(_p(q), _p(k), _p(v), _p(bh, _I64),
+                                        _p(rows, _I64), n, _p(o), _p(lse), B,
+                                        H, N, D, float(scale),
+                                        int(bool(causal))), "fwd_rows")
+    return o, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens, scale: float, causal: bool):
+    """Packed forward.  q, k, v: [H, total, D]; cu_seqlens int [nseq+1].
+
+    Returns (O [H, total, D], L [H, total]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    H, total, D = q.shape
+    cu = np.ascontiguousarray(_i32(cu_seqlens))
+    o = np.empty_like(q)
+    lse = np.empty((H, total), dtype=np.float64)
+    _check(_load().oracle_attn_fwd_varlen(_p(q), _p(k), _p(v), _p(o), _p(lse),
+                                          _p(cu, _I32), cu.shape[0] - 1, H,
+                                          total, D, float(scale),
+                                          int(bool(causal))), "fwd_varlen")
+    return o, lse
+
+
+def fwd_varlen_rows(q, k, v, cu_seqlens, scale: float, causal: bool, heads,
+                    tokens):
+    """Selected rows of the packed forward: (heads[t], packed token tokens[t])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    H, total, D = q.shape
+    cu = np.ascontiguousarray(_i32(cu_seqlens))
+    heads = np.ascontiguousarray(heads, dtype=np.int64)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+    n = heads.shape[0]
+    o = np.empty((n, D), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    _check(_load().oracle_attn_fwd_varlen_rows(
+        _p(q), _p(k), _p(v), _p(cu, _I32), cu.shape[0] - 1, H, total, D,
+        float(scale), int(bool(causal)), _p(heads, _I64), _p(tokens, _I64), n,
+        _p(o), _p(lse)), "fwd_varlen_rows")
+    return o, lse
+
+
+def bwd(q, k, v, dout, scale: float, causal: bool):
+    """Dense backward: gradients of <dout, O> w.r.t. q, k, v ([B,H,N,D] each)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, D = q.shape
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    _check(_load().oracle_attn_bwd(_p(q), _p(k), _p(v), _p(dout), _p(dq),
+                                   _p(dk), _p(dv), B, H, N, D, float(scale),
+                                   int(bool(causal))), "bwd")
+    return dq, dk, dv
+
+
+def _i32(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.asarray(x, dtype=np.int32)

@@ -1,0 +1,373 @@
+"""Pins for the fp64 oracle: checks against what the pages and mathematics fix.
+
+Every check here is independent of the oracle's own code path: closed forms,
+invariants the pages state, special cases that reduce to a library routine
+(scipy's logsumexp, torch's CPU scaled_dot_product_attention and autograd),
+central finite differences, and 50-digit mpmath on tiny inputs.
+"""
+import math
+import os
+
+import mpmath
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import attn_inputs
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, val = line.split("=")
+            out[key.strip()] = [float(x) for x in val.split()]
+    return out
+
+
+def _one_query(scores):
+    """Inputs whose single query row has exactly the given scores (scale 1).
+
+    D = len(scores); q = e0, k_j = scores[j] * e0, v_j = e_j, so O = P.
+    """
+    n = len(scores)
+    q = np.zeros((1, 1, 1, n))
+    q[0, 0, 0, 0] = 1.0
+    k = np.zeros((1, 1, n, n))
+    k[0, 0, :, 0] = scores
+    v = np.eye(n)[None, None]
+    # the oracle's dense layout has equal Q and K lengths: pad Q with copies
+    q = np.repeat(q, n, axis=2)
+    return q, k, v
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# --------------------------------------------------------------------------
+# P1: the split-tile example of tensortonic section 4.
+# --------------------------------------------------------------------------
+def test_split_tile_example_one_normalisation():
+    g = _golden("split_tile_1234.txt")
+    scores, t0, t1 = g["scores"], g["tile0"], g["tile1"]
+    assert t0 + t1 == scores
+    q, k, v = _one_query(scores)
+    o, lse = oracle.fwd(q, k, v, scale=1.0, causal=False)
+    p = o[0, 0, 0]
+    mpmath.mp.dps = 40
+    ex = [mpmath.e ** mpmath.mpf(s) for s in scores]
+    tot = mpmath.fsum(ex)
+    # closed form of softmax of [1, 2, 3, 4] and of its log-sum-exp
+    for j in range(4):
+        assert abs(p[j] - float(ex[j] / tot)) < 1e-15
+    assert abs(lse[0, 0, 0] - float(mpmath.log(tot))) < 1e-14
+    assert abs(p.sum() - 1.0) < 1e-15
+    # the wrong per-tile softmax gives each tile a full unit of weight; the
+    # correct weights give the tiles very different shares
+    share0, share1 = p[:2].sum(), p[2:].sum()
+    assert abs(share0 - float((ex[0] + ex[1]) / tot)) < 1e-15
+    assert share0 < 0.2 and share1 > 0.8
+    tile_local = np.concatenate([scipy.special.softmax(t0),
+                                 scipy.special.softmax(t1)])
+    assert abs(tile_local.sum() - 2.0) < 1e-15
+    assert np.abs(tile_local - p).max() > 0.1
+    assert np.abs(0.5 * tile_local - p).max() > 0.1  # averaging does not fix it
+
+
+def test_split_tile_example_running_softmax_agrees():
+    """The running-softmax rule (tensortonic section 5), applied tile by tile
+    in 40-digit arithmetic, reaches the oracle's one-pass weights and L."""
+    g = _golden("split_tile_1234.txt")
+    q, k, v = _one_query(g["scores"])
+    o, lse = oracle.fwd(q, k, v, scale=1.0, causal=False)
+    mpmath.mp.dps = 40
+    m, l, u = mpmath.mpf("-inf"), mpmath.mpf(0), [mpmath.mpf(0)] * 4
+    for tile, cols in ((g["tile0"], (0, 1)), (g["tile1"], (2, 3))):
+        m_new = max(m, max(mpmath.mpf(s) for s in tile))
+        a = mpmath.e ** (m - m_new) if m != mpmath.mpf("-inf") else 0
+        e = [mpmath.e ** (mpmath.mpf(s) - m_new) for s in tile]
+        l = a * l + sum(e)
+        u = [a * x for x in u]
+        for c, w in zip(cols, e):
+            u[c] += w  # value vectors are one-hot
+        m = m_new
+    for j in range(4):
+        assert abs(o[0, 0, 0, j] - float(u[j] / l)) < 1e-15
+    assert abs(lse[0, 0, 0] - float(m + mpmath.log(l))) < 1e-14
+    # the per-tile log-sum-exps merge into the full one
+    lse_t = [scipy.special.logsumexp(g["tile0"]),
+             scipy.special.logsumexp(g["tile1"])]
+    assert abs(np.logaddexp(*lse_t) - lse[0, 0, 0]) < 1e-14
+
+
+# --------------------------------------------------------------------------
+# P2/P3: weights sum to one; constant values come back unchanged.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_values_return_themselves(causal):
+    B, H, N, D = 2, 3, 37, 8
+    q, k = _rand((B, H, N, D), 1), _rand((B, H, N, D), 2)
+    c = _rand((D,), 3)
+    v = np.broadcast_to(c, (B, H, N, D)).copy()
+    o, _ = oracle.fwd(q, k, v, 0.35, causal)
+    assert np.abs(o - c).max() <= 1e-14 * np.abs(c).max() * 4
+    ones = np.ones((B, H, N, D))
+    o1, _ = oracle.fwd(q, k, ones, 0.35, causal)  # row sums of P
+    assert np.abs(o1 - 1.0).max() < 1e-13
+
+
+# --------------------------------------------------------------------------
+# P4/P8: causal row 0 reads only key 0; N = 1; shift and permutation.
+# --------------------------------------------------------------------------
+def test_causal_row0_and_single_token():
+    B, H, N, D = 1, 2, 9, 5
+    q, k, v = (_rand((B, H, N, D), s) for s in (4, 5, 6))
+    scale = 0.7
+    o, lse = oracle.fwd(q, k, v, scale, True)
+    for h in range(H):
+        assert np.array_equal(o[0, h, 0], v[0, h, 0])
+        s00 = scale * math.fsum(q[0, h, 0] * k[0, h, 0])
+        assert abs(lse[0, h, 0] - s00) < 1e-15
+    o1, l1 = oracle.fwd(q[:, :, :1], k[:, :, :1], v[:, :, :1], scale, False)
+    assert np.array_equal(o1[0, :, 0], v[0, :, 0])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_score_shift_moves_lse_only(causal):
+    """Adding c to every key adds scale*<q_i, c> to every score of row i:
+    weights are unchanged (stable softmax, tensortonic section 4) and L moves
+    by exactly that amount."""
+    B, H, N, D = 1, 2, 23, 6
+    q, k, v = (_rand((B, H, N, D), s) for s in (7, 8, 9))
+    c = _rand((D,), 10)
+    scale = 0.4
+    o, lse = oracle.fwd(q, k, v, scale, causal)
+    o2, lse2 = oracle.fwd(q, k + c, v, scale, causal)
+    shift = scale * np.einsum("bhnd,d->bhn", q, c)
+    assert np.abs(o2 - o).max() < 1e-12
+    assert np.abs(lse2 - lse - shift).max() < 1e-12
+
+
+def test_key_value_permutation_invariance_noncausal():
+    B, H, N, D = 1, 1, 19, 7
+    q, k, v = (_rand((B, H, N, D), s) for s in (11, 12, 13))
+    perm = np.random.default_rng(14).permutation(N)
+    o, lse = oracle.fwd(q, k, v, 0.3, False)
+    o2, lse2 = oracle.fwd(q, k[:, :, perm], v[:, :, perm], 0.3, False)
+    assert np.abs(o2 - o).max() < 1e-13
+    assert np.abs(lse2 - lse).max() < 1e-13
+
+
+def test_outputs_are_convex_combinations():
+    B, H, N, D = 2, 2, 31, 4
+    q, k, v = (_rand((B, H, N, D), s) for s in (15, 16, 17))
+    for causal in (False, True):
+        o, _ = oracle.fwd(q, k, v, 1.3, causal)
+        for i in range(N):
+            kv = v[:, :, : (i + 1 if causal else N)]
+            assert (o[:, :, i] <= kv.max(axis=2) + 1e-13).all()
+            assert (o[:, :, i] >= kv.min(axis=2) - 1e-13).all()
+
+
+# --------------------------------------------------------------------------
+# P5/P10: L is the log-sum-exp of the row; exp(s - L) recovers the weights.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_is_logsumexp_and_recomputes_weights(causal):
+    B, H, N, D = 1, 2, 16, 16  # D >= N: one-hot values expose P itself
+    q, k = _rand((B, H, N, D), 18), _rand((B, H, N, D), 19)
+    v = np.broadcast_to(np.eye(N, D), (B, H, N, D)).copy()
+    scale = 0.45
+    o, lse = oracle.fwd(q, k, v, scale, causal)
+    s = scale * np.matmul(q, np.swapaxes(k, -1, -2))
+    for h in range(H):
+        for i in range(N):
+            n = i + 1 if causal else N
+            ref = scipy.special.logsumexp(s[0, h, i, :n])
+            assert abs(lse[0, h, i] - ref) < 1e-13
+            p = o[0, h, i, :N]
+            assert np.abs(p[:n] - np.exp(s[0, h, i, :n] - lse[0, h, i])).max() < 1e-14
+            assert np.abs(p[n:]).max(initial=0.0) == 0.0
+
+
+# --------------------------------------------------------------------------
+# P6: 50-digit brute force on tiny inputs.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1), (1, 2, 5, 3), (2, 1, 8, 4)])
+def test_mpmath_brute_force(shape, causal):
+    q, k, v = (_rand(shape, s) for s in (20, 21, 22))
+    scale = 0.6
+    o, lse = oracle.fwd(q, k, v, scale, causal)
+    mpmath.mp.dps = 50
+    B, H, N, D = shape
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                n = i + 1 if causal else N
+                s = [mpmath.mpf(scale) * mpmath.fsum(
+                    mpmath.mpf(q[b, h, i, d]) * mpmath.mpf(k[b, h, j, d])
+                    for d in range(D)) for j in range(n)]
+                w = [mpmath.e ** x for x in s]
+                tot = mpmath.fsum(w)
+                for d in range(D):
+                    ref = mpmath.fsum(w[j] * mpmath.mpf(v[b, h, j, d])
+                                      for j in range(n)) / tot
+                    assert abs(o[b, h, i, d] - float(ref)) <= 1e-13 * (1 + abs(float(ref)))
+                assert abs(lse[b, h, i] - float(mpmath.log(tot))) < 1e-13
+
+
+# --------------------------------------------------------------------------
+# P7: a library routine in the special case it covers (equal lengths).
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,D", [(1, 64), (63, 64), (129, 128), (300, 64)])
+def test_matches_torch_sdpa_fp64(N, D, causal):
+    g = torch.Generator().manual_seed(N * 7 + D)
+    q, k, v = (torch.randn(2, 2, N, D, generator=g, dtype=torch.float64)
+               for _ in range(3))
+    scale = 1.0 / math.sqrt(D)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, is_causal=causal, scale=scale).numpy()
+    o, _ = oracle.fwd(q, k, v, scale, causal)
+    assert np.abs(o - ref).max() < 1e-12
+
+
+# --------------------------------------------------------------------------
+# Selected-row and packed entry points agree with the dense forward.
+# --------------------------------------------------------------------------
+def test_rows_and_varlen_agree_with_dense():
+    B, H, N, D = 2, 3, 41, 8
+    q, k, v = (_rand((B, H, N, D), s) for s in (23, 24, 25))
+    for causal in (False, True):
+        o, lse = oracle.fwd(q, k, v, 0.5, causal)
+        bh = np.array([0, 5, 3, 2, 4])
+        rows = np.array([0, 40, 17, 1, 39])
+        orows, lrows = oracle.fwd_rows(q, k, v, 0.5, causal, bh, rows)
+        of, lf = o.reshape(B * H, N, D), lse.reshape(B * H, N)
+        assert np.array_equal(orows, of[bh, rows])
+        assert np.array_equal(lrows, lf[bh, rows])
+    # packing: sequences of lengths 5, 0, 17, 1 behave as independent runs
+    lengths = [5, 0, 17, 1]
+    cu = attn_inputs.cu_seqlens(lengths).numpy()
+    total = int(cu[-1])
+    qp, kp, vp = (_rand((H, total, D), s) for s in (26, 27, 28))
+    for causal in (False, True):
+        o, lse = oracle.fwd_varlen(qp, kp, vp, cu, 0.5, causal)
+        for b, n in enumerate(lengths):
+            if n == 0:
+                continue
+            sl = slice(cu[b], cu[b + 1])
+            od, ld = oracle.fwd(qp[None, :, sl], kp[None, :, sl],
+                                vp[None, :, sl], 0.5, causal)
+            assert np.array_equal(o[:, sl], od[0])
+            assert np.array_equal(lse[:, sl], ld[0])
+        heads = np.array([0, 2, 1, 2])
+        toks = np.array([0, 4, 5, total - 1])
+        orow, lrow = oracle.fwd_varlen_rows(qp, kp, vp, cu, 0.5, causal,
+                                            heads, toks)
+        assert np.array_equal(orow, o[heads, toks])
+        assert np.array_equal(lrow, lse[heads, toks])
+
+
+# --------------------------------------------------------------------------
+# P11: the stability variant (Q * 8) of the tiny workload.
+# --------------------------------------------------------------------------
+def test_stability_variant_large_scores():
+    q, k, v, q8 = attn_inputs.tiny_inputs()
+    scale = attn_inputs.TINY.scale
+    raw = torch.matmul(q8.double(), k.double().transpose(-1, -2))
+    assert raw.abs().max() > 100  # raw scores exceed 100
+    # exp of a raw score this large overflows fp32 (max ~ e^88.7): only the
+    # max-subtraction of the stable softmax keeps the weights finite
+    assert float(raw.max()) > 88.8
+    o, lse = oracle.fwd(q8, k, v, scale, False)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    mpmath.mp.dps = 50
+    q8d, kd, vd = (x.double().numpy()[0, 0] for x in (q8, k, v))
+    for i in (0, 17, 64, 127):
+        s = [mpmath.mpf(scale) * mpmath.fsum(
+            mpmath.mpf(a) * mpmath.mpf(b) for a, b in zip(q8d[i], kd[j]))
+            for j in range(128)]
+        w = [mpmath.e ** x for x in s]
+        tot = mpmath.fsum(w)
+        assert abs(lse[0, 0, i] - float(mpmath.log(tot))) < 1e-12
+        for d in (0, 31, 63):
+            ref = float(mpmath.fsum(w[j] * mpmath.mpf(vd[j, d])
+                                    for j in range(128)) / tot)
+            assert abs(o[0, 0, i, d] - ref) < 1e-13
+
+
+# --------------------------------------------------------------------------
+# P9: backward.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_finite_differences(causal):
+    B, H, N, D = 1, 2, 6, 3
+    q, k, v, do = (_rand((B, H, N, D), s) for s in (30, 31, 32, 33))
+    scale = 0.8
+    dq, dk, dv = oracle.bwd(q, k, v, do, scale, causal)
+
+    def f(qq, kk, vv):
+        o, _ = oracle.fwd(qq, kk, vv, scale, causal)
+        return float(np.sum(o * do))
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            fp = f(args["q"], args["k"], args["v"])
+            args[name] = xm
+            fm = f(args["q"], args["k"], args["v"])
+            num[idx] = (fp - fm) / (2 * h)
+        err = np.linalg.norm(num - g) / np.linalg.norm(g)
+        assert err < 1e-6, (name, err)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_autograd_and_invariants(causal):
+    B, H, N, D = 2, 2, 70, 16
+    g = torch.Generator().manual_seed(34)
+    q, k, v, do = (torch.randn(B, H, N, D, generator=g, dtype=torch.float64)
+                   for _ in range(4))
+    scale = 0.25
+    qa, ka, va = (x.clone().requires_grad_(True) for x in (q, k, v))
+    s = scale * torch.matmul(qa, ka.transpose(-1, -2))
+    if causal:
+        s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1),
+                          float("-inf"))
+    o = torch.matmul(torch.softmax(s, dim=-1), va)
+    o.backward(do)
+    dq, dk, dv = oracle.bwd(q, k, v, do, scale, causal)
+    for ref, got in ((qa.grad, dq), (ka.grad, dk), (va.grad, dv)):
+        ref = ref.numpy()
+        assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 1e-12
+    # softmax is shift-invariant in the keys: sum_j dK_j = 0
+    assert np.abs(dk.sum(axis=2)).max() < 1e-11
+    # rows of P sum to one: sum_j dV_j = sum_i dO_i
+    assert np.abs(dv.sum(axis=2) - do.numpy().sum(axis=2)).max() < 1e-11
+
+
+def test_input_generators_are_seeded_bf16():
+    a = attn_inputs.randn_bf16((2, 3, 5, 8), 7)
+    b = attn_inputs.randn_bf16((2, 3, 5, 8), 7)
+    assert a.dtype == torch.bfloat16 and torch.equal(a, b)
+    c = attn_inputs.randn_bf16((2, 3, 5, 8), 7, chunk_rows=4)
+    assert c.shape == a.shape and torch.isfinite(c.float()).all()
+    lengths = attn_inputs.varlen_lengths(2)
+    assert len(lengths) == 16 and all(128 <= n <= 8192 for n in lengths)
+    cu = attn_inputs.cu_seqlens(lengths)
+    assert cu.dtype == torch.int32 and int(cu[-1]) == sum(lengths)
