@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one causal forward pass (fa_fwd) over the workload B4 H32 N4096
+D128 bf16 (iid N(0,1) inputs, scale 1/sqrt(128)), inputs resident in HBM.
+Prints ONE JSON line with the throughput in TFLOP/s, the roofline position of
+the forward kernel, the backward pass (fa_bwd, B2 H32 N4096 D128 causal)
+against the same roofline, and the fp64 CPU oracle timed on a bounded sample
+of the same workload.
+
+FLOP convention: 4*D flops per (query, key) pair, causal counted as half of
+B*H*N^2 pairs; backward counted as 2.5x forward; softmax work not counted.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s & % bf16 MFMA peak, causal B4 H32 N4096 D128"
+# MI355X dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 flop/clk/CU
+PEAK_BF16_TFLOPS = 2516.6
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_causal_b4h32n4096d128_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_io_aware_44_amd", "csrc", f)
+                  for f in ("fa_fwd.hip", "fa_device.hpp")]
+
+
+def log(*a):
+    print("bench:", *a, file=sys.stderr, flush=True)
+
+
+def fwd_flops(B, H, N, D, causal):
+    return 4.0 * B * H * N * N * D * (0.5 if causal else 1.0)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per forward launch from the committed rocprofv3 counter
+    summary, or None when absent or taken on different kernel sources."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    src = re.search(r"^source_hash:\s*(\S+)", text, re.M)
+    val = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return float(val.group(1))
+
+
+def time_launches(torch, fn, steps, warmup):
+    """Warm up, then time exactly `steps` calls: whole-region elapsed time
+    and per-launch durations, all with HIP events on the launch stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for s, e in ev:
+        s.record()
+        fn()
+        e.record()
+    t1.record()
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1)
+    per = [s.elapsed_time(e) for s, e in ev]
+    return total, per
+
+
+def cpu_baseline(budget_s: float):
+    """The fp64 oracle, untuned, on whole (batch, head) slices of the causal
+    workload, taken in order until about budget_s seconds of CPU work."""
+    import attn_inputs as ai
+    import oracle
+    w = ai.CAUSAL
+    q, k, v = ai.qkv(w.B, w.H, w.N, w.D, w.seed)
+    per_head = fwd_flops(1, 1, w.N, w.D, True)
+    done, elapsed = 0, 0.0
+    for bh in range(w.B * w.H):
+        b, h = divmod(bh, w.H)
+        args = [x[b, h][None, None].double().numpy() for x in (q, k, v)]
+        t = time.perf_counter()
+        oracle.fwd(*args, w.scale, True)
+        elapsed += time.perf_counter() - t
+        done += 1
+        if elapsed >= budget_s:
+            break
+    return {
+        "value": per_head * done / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "%d of %d (batch, head) slices of causal B4 H32 N4096 D128, "
+                  "every row, fp64, %.1f s" % (done, w.B * w.H, elapsed),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--bwd-steps", type=int, default=10)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(heads would shard across GPUs with no exchange); run --gpus 1",
+              file=sys.stderr)
+        return 2
+    rank = int(os.environ.get("RANK", "0"))
+
+    import torch
+    import attn_inputs as ai
+    import exact_io_aware_44_amd as fa
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    fa.load()
+
+    # ---- forward: the metric -------------------------------------------------
+    w = ai.CAUSAL
+    log("inputs", w.name)
+    q, k, v = (x.cuda() for x in ai.qkv(w.B, w.H, w.N, w.D, w.seed))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+
+    def fwd_step():
+        fa.fa_fwd(q, k, v, softmax_scale=w.scale, causal=True, out=o, lse=lse)
+
+    log("forward: %d warmup, %d timed" % (args.warmup, args.steps))
+    total_ms, per = time_launches(torch, fwd_step, args.steps, args.warmup)
+    flops = fwd_flops(w.B, w.H, w.N, w.D, True)
+    ms_per_step = total_ms / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    launch_ms = statistics.mean(per)
+    achieved = flops / (launch_ms * 1e-3) / 1e12
+    del q, k, v, o, lse
+
+    # ---- backward against the same roofline ---------------------------------
+    wb = ai.BACKWARD
+    log("backward", wb.name)
+    qb, kb, vb, dob = (x.cuda() for x in ai.backward_inputs())
+    ob, lseb = fa.fa_fwd(qb, kb, vb, softmax_scale=wb.scale, causal=True)
+    dq, dk, dv = (torch.empty_like(qb) for _ in range(3))
+    ws = torch.empty(fa.fa_bwd_workspace_size(wb.B, wb.H, wb.N, wb.D),
+                     dtype=torch.uint8, device="cuda")
+
+    def bwd_step():
+        fa.fa_bwd(qb, kb, vb, ob, lseb, dob, softmax_scale=wb.scale, causal=True,
+                  dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    btotal, bper = time_launches(torch, bwd_step, args.bwd_steps, 3)
+    bflops = 2.5 * fwd_flops(wb.B, wb.H, wb.N, wb.D, True)
+    b_ms = btotal / args.bwd_steps
+    backward = {"workload": wb.name, "ms": round(b_ms, 4),
+                "tflops": round(bflops / (b_ms * 1e-3) / 1e12, 2),
+                "frac": round(bflops / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "flops_per_call": bflops, "launches": 3}
+    del qb, kb, vb, dob, ob, lseb, dq, dk, dv, ws
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H,
+                   "seq_len": w.N, "head_dim": w.D, "causal": True,
+                   "flops_per_step": flops,
+                   "flop_convention": "4*D per (query,key) pair; causal = half of B*H*N^2"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(),
+                     "kernel": "fwd_kernel<128, causal>",
+                     "avg_launch_ms": round(launch_ms, 5)},
+        "backward": backward,
+    }
+    if rank == 0 and args.cpu_budget > 0:
+        log("cpu baseline (oracle), about %.0f s" % args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    if rank == 0:
+        print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,188 @@
+"""Exact, IO-aware tiled softmax attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding of ``libfa.so`` (C ABI in ``include/fa.h``).  Every
+function here only marshals arguments: it checks tensor dtype, device and
+shape, allocates outputs with torch when the caller passes none, and hands raw
+device pointers plus the current HIP stream to the library.  All arithmetic
+runs in the library's HIP kernels; there is no CPU or PyTorch fallback, and a
+missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["load", "build", "FaError", "fa_fwd", "fa_fwd_varlen", "fa_bwd",
+           "fa_bwd_workspace_size", "fa_status_string", "LIB_PATH"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+_lib = None
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+
+
+class FaError(RuntimeError):
+    """A non-zero fa_status returned by the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        super().__init__("%s: %s" % (where, fa_status_string(status)))
+
+
+def build() -> str:
+    """Compile libfa.so for gfx950 (always recompiles)."""
+    from . import buildlib
+    return buildlib.build()
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so (building it first if it is absent) and declare the ABI."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.fa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]
+    lib.fa_fwd.restype = _i
+    lib.fa_fwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
+                                  _i, _f, _i, _vp]
+    lib.fa_fwd_varlen.restype = _i
+    lib.fa_bwd_workspace_size.argtypes = [_i, _i, _i, _i]
+    lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                           ctypes.c_size_t, _i, _i, _i, _i, _f, _i, _vp]
+    lib.fa_bwd.restype = _i
+    lib.fa_status_string.argtypes = [_i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def fa_bwd_workspace_size(B: int, H: int, N: int, D: int) -> int:
+    return int(load().fa_bwd_workspace_size(B, H, N, D))
+
+
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _check(t, name, shape=None):
+    torch = _torch()
+    if t.dtype != torch.bfloat16:
+        raise TypeError("%s must be bfloat16, got %s" % (name, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape),
+                                                         tuple(shape)))
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _scale(scale, D):
+    return 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+
+def fa_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None,
+           return_lse=True, stream=None):
+    """Forward pass.  q, k, v: bf16 [B, H, N, D] on the GPU.
+
+    Returns (o, lse): o bf16 [B, H, N, D] and lse fp32 [B, H, N] (natural-log
+    row log-sum-exp of the scaled scores), or (o, None) with
+    ``return_lse=False``.  ``softmax_scale`` defaults to 1/sqrt(D).
+    """
+    torch = _torch()
+    _check(q, "q")
+    B, H, N, D = q.shape
+    _check(k, "k", q.shape)
+    _check(v, "v", q.shape)
+    o = torch.empty_like(q) if out is None else out
+    _check(o, "out", q.shape)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    rc = load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, D,
+                       _scale(softmax_scale, D), int(bool(causal)), _stream(stream))
+    if rc != 0:
+        raise FaError(rc, "fa_fwd")
+    return o, lse
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None,
+                  causal=False, out=None, lse=None, return_lse=True, stream=None):
+    """Packed forward.  q, k, v: bf16 [H, total, D]; cu_seqlens: int32 GPU
+    tensor [nseq + 1]; max_seqlen: host int >= the longest sequence.
+
+    Returns (o [H, total, D] bf16, lse [H, total] fp32 or None).
+    """
+    torch = _torch()
+    _check(q, "q")
+    H, total, D = q.shape
+    _check(k, "k", q.shape)
+    _check(v, "v", q.shape)
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 GPU tensor")
+    nseq = cu_seqlens.shape[0] - 1
+    o = torch.empty_like(q) if out is None else out
+    _check(o, "out", q.shape)
+    if lse is None and return_lse:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    rc = load().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                              _ptr(cu_seqlens), nseq, total, int(max_seqlen), H, D,
+                              _scale(softmax_scale, D), int(bool(causal)),
+                              _stream(stream))
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_varlen")
+    return o, lse
+
+
+def fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None,
+           dk=None, dv=None, workspace=None, stream=None):
+    """Backward pass.  o and lse must come from fa_fwd on the same inputs.
+
+    Returns (dq, dk, dv), bf16 [B, H, N, D].  ``workspace`` (uint8 GPU tensor
+    of at least fa_bwd_workspace_size bytes) is allocated when not given.
+    """
+    torch = _torch()
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check(t, name, q.shape)
+    B, H, N, D = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    ws_bytes = fa_bwd_workspace_size(B, H, N, D)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    rc = load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                       workspace.numel() * workspace.element_size(), B, H, N, D,
+                       _scale(softmax_scale, D), int(bool(causal)), _stream(stream))
+    if rc != 0:
+        raise FaError(rc, "fa_bwd")
+    return dq, dk, dv

@@ -1,0 +1,124 @@
+// fa_api.cpp -- the C ABI declared in include/fa.h: argument validation
+// (completed before any HIP call, so every rejection is side-effect free and
+// testable without a GPU), then dispatch to the kernel launchers.
+#include "../../include/fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxSliceBytes = (int64_t)1 << 31;  // 32-bit offsets per slice
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(int H, int D, float scale, int causal) {
+    if (H < 1) return FA_ERR_SHAPE;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_ARG;
+    return FA_OK;
+}
+
+int check_slice(int64_t tokens, int D) {
+    // the kernels also address up to one tile past the end; keep headroom
+    return (tokens + 256) * D * 2 < kMaxSliceBytes ? FA_OK : FA_ERR_TOO_LARGE;
+}
+
+int validate_fwd(const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, int B, int H, int N, int D, float scale,
+                 int causal) {
+    if (!q || !k || !v || !o) return FA_ERR_NULL;
+    if (B < 1 || N < 1) return FA_ERR_SHAPE;
+    if (int rc = check_common(H, D, scale, causal)) return rc;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        (lse && !aligned16(lse)))
+        return FA_ERR_ALIGN;
+    if (B > 65535 || H > 65535) return FA_ERR_SHAPE;  // grid y / z limits
+    return check_slice(N, D);
+}
+
+size_t workspace_bytes(int B, int H, int N) {
+    const size_t rows = (size_t)B * H * N;
+    return (rows * sizeof(float) + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+        case FA_ERR_SHAPE: return "FA_ERR_SHAPE: a size argument is out of range";
+        case FA_ERR_UNSUPPORTED:
+            return "FA_ERR_UNSUPPORTED: head width must be 64 or 128 and causal 0 or 1";
+        case FA_ERR_ALIGN: return "FA_ERR_ALIGN: pointers must be 16-byte aligned";
+        case FA_ERR_WORKSPACE:
+            return "FA_ERR_WORKSPACE: workspace is NULL or smaller than fa_bwd_workspace_size";
+        case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: a kernel launch failed";
+        case FA_ERR_ARG: return "FA_ERR_ARG: softmax_scale must be finite and > 0";
+        case FA_ERR_TOO_LARGE:
+            return "FA_ERR_TOO_LARGE: one (batch, head) slice exceeds 2 GiB";
+        default: return "unknown fa status";
+    }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int D, float softmax_scale, int causal,
+           hipStream_t stream) {
+    if (int rc = validate_fwd(q, k, v, o, lse, B, H, N, D, softmax_scale, causal))
+        return rc;
+    fa::FwdArgs a{q, k, v, o, lse, nullptr, B, H, N, N, D, softmax_scale, causal != 0};
+    return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                  float* lse, const int32_t* cu_seqlens, int nseq, int total,
+                  int max_seqlen, int H, int D, float softmax_scale, int causal,
+                  hipStream_t stream) {
+    if (!q || !k || !v || !o || !cu_seqlens) return FA_ERR_NULL;
+    if (nseq < 1 || total < 1 || max_seqlen < 1 || nseq > 65535) return FA_ERR_SHAPE;
+    if (int rc = check_common(H, D, softmax_scale, causal)) return rc;
+    if (H > 65535) return FA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        (lse && !aligned16(lse)) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+        return FA_ERR_ALIGN;
+    if (int rc = check_slice(total, D)) return rc;
+    if (max_seqlen > total) max_seqlen = total;  // no sequence is longer than total
+    fa::FwdArgs a{q, k, v, o, lse, cu_seqlens, nseq, H, total, max_seqlen, D,
+                  softmax_scale, causal != 0};
+    return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int D) {
+    if (B < 1 || H < 1 || N < 1 || (D != 64 && D != 128)) return 0;
+    return workspace_bytes(B, H, N);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+           void* workspace, size_t ws_bytes, int B, int H, int N, int D,
+           float softmax_scale, int causal, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+    if (B < 1 || N < 1) return FA_ERR_SHAPE;
+    if (int rc = check_common(H, D, softmax_scale, causal)) return rc;
+    if (B > 65535 || H > 65535) return FA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+        !aligned16(dv))
+        return FA_ERR_ALIGN;
+    if (int rc = check_slice(N, D)) return rc;
+    if (!workspace || ws_bytes < workspace_bytes(B, H, N)) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace),
+                  B, H, N, D, softmax_scale, causal != 0};
+    return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// fa_device.hpp -- device-side building blocks for the gfx950 attention
+// kernels: vector types, range-checked buffer loads/stores, the bf16 MFMA and
+// the LDS transpose read.
+//
+// Register layouts used throughout (verified on gfx950 with an in-bounds
+// probe of the builtins):
+//
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds A[l % 32][8*(l/32) + j],          j = 0..7
+//     B: lane l holds B[8*(l/32) + j][l % 32],          j = 0..7
+//     D: lane l, register r holds D[8*(r/4) + 4*(l/32) + r%4][l % 32]
+//
+//   ds_read_b64_tr_b16 (per 16-lane group; lane i of the group supplies an
+//   address of four 16-bit values c_i[0..3]):
+//     lane l receives { c_{4j + (l%16)/4}[l % 4] : j = 0..3 }
+//   So if lane i addresses row R + i/4, column C + 4*(i%4) of a row-major
+//   bf16 matrix, lane l receives the column C + l%16 of rows R..R+3: a
+//   row-major tile becomes a column-major MFMA operand without a transposed
+//   copy in LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// ---- range-checked buffer access ------------------------------------------
+// A buffer resource covers [base, base + bytes); loads outside return zero and
+// stores outside are dropped, which handles ragged tiles without branches.
+struct Buf {
+    __amdgpu_buffer_rsrc_t r;
+};
+
+__device__ __forceinline__ Buf make_buf(const void* base, uint32_t bytes) {
+    // word 3 = 0x00020000: raw 32-bit dword format for the gfx9 family
+    return Buf{__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base),
+                                                 (short)0, (int)bytes,
+                                                 0x00020000)};
+}
+
+__device__ __forceinline__ u32x4 load16(Buf b, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(b.r, off, 0, 0);
+}
+__device__ __forceinline__ void store16(Buf b, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, b.r, off, 0, 0);
+}
+__device__ __forceinline__ void store8(Buf b, uint32_t off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, b.r, off, 0, 0);
+}
+__device__ __forceinline__ void store4(Buf b, uint32_t off, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, b.r, off, 0, 0);
+}
+__device__ __forceinline__ float loadf(Buf b, uint32_t off) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_raw_buffer_load_b32(b.r, off, 0, 0));
+}
+
+// ---- MFMA ------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- LDS -------------------------------------------------------------------
+__device__ __forceinline__ bf16x8 lds_read16(const bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void lds_write16(bf16* p, u32x4 v) {
+    *reinterpret_cast<u32x4*>(p) = v;
+}
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+    i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// ---- conversions / math ----------------------------------------------------
+__device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }  // RNE
+__device__ __forceinline__ float exp2_fast(float x) {
+    return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
+}
+__device__ __forceinline__ float log2_fast(float x) {
+    return __builtin_amdgcn_logf(x);  // v_log_f32 (base 2)
+}
+__device__ __forceinline__ float xor32(float x) {  // value of lane l ^ 32
+    return __shfl_xor(x, 32, 64);
+}
+__device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
+    bf16x4 v{to_bf16(a), to_bf16(b), to_bf16(c), to_bf16(d)};
+    return __builtin_bit_cast(u32x2, v);
+}
+
+}  // namespace fa

@@ -1,0 +1,46 @@
+// fa_launch.hpp -- internal interface between the C ABI (fa_api.cpp) and the
+// kernel launchers.  Arguments are already validated; every launcher returns
+// the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;             // may be null
+    const int32_t* cu;      // packed offsets (varlen) or null (dense)
+    int B;                  // batch (dense) or number of sequences (varlen)
+    int H;
+    int N;                  // tokens per sequence (dense) or packed total
+    int max_seqlen;         // longest sequence (== N when dense)
+    int D;
+    float scale;
+    bool causal;
+};
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const float* lse;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dsum;            // workspace: [B, H, N] fp32
+    int B, H, N, D;
+    float scale;
+    bool causal;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+}  // namespace fa

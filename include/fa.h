@@ -1,0 +1,151 @@
+/*
+ * fa.h -- exact, IO-aware tiled softmax attention for AMD Instinct MI355X
+ * (gfx950): the C ABI of libfa.so.
+ *
+ * The library computes exact softmax attention (FlashAttention; tensortonic
+ * "FlashAttention" sections 3-7, ai-engineering wiki "Trick: Numerical
+ * Stability with Softmax") without ever writing the N x N score or weight
+ * matrix to device memory:
+ *
+ *     O_i = sum_j softmax_j(scale * <q_i, k_j>) v_j      over allowed keys j
+ *     L_i = m_i + ln(l_i)                                (row log-sum-exp)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Element types: q, k, v, o, dout, dq, dk, dv are bfloat16 (raw 16-bit
+ *    storage, round-to-nearest-even on output); lse is float32.  Arithmetic
+ *    is bf16 x bf16 products with float32 accumulation.
+ *  - Dense layout: [B, H, N, D] row-major, contiguous (tensortonic section 9:
+ *    [batch, heads, tokens, head_width]); lse is [B, H, N].  Q, K and V have
+ *    the same length N.
+ *  - Causal masking (causal = 1) lets query i read keys j <= i (a token reads
+ *    itself and the past, never the future: tensortonic section 1).
+ *  - softmax_scale multiplies the float32 dot product q_i . k_j before the
+ *    softmax (tensortonic section 6 divides by sqrt(head width); pass
+ *    1/sqrt(D) for that).  It must be finite and > 0.
+ *  - L is in natural-log units of the scaled scores: L_i = ln sum_j
+ *    exp(scale * q_i . k_j) over the allowed keys (tensortonic section 7).
+ *  - Supported head widths: D = 64 and D = 128.
+ *  - Pointers are device pointers owned by the caller, 16-byte aligned.  The
+ *    library never allocates, frees or keeps them after the call returns.
+ *  - Every call is asynchronous on `stream` (0 = the null stream) and never
+ *    synchronises; results are valid once the caller has synchronised the
+ *    stream.  Calls on different streams touching disjoint outputs may run
+ *    concurrently.
+ *  - Errors: every argument check completes before any HIP call, so a
+ *    rejected call has no side effect.  After validation the only error is
+ *    FA_ERR_LAUNCH (the launch itself failed).  Faults inside a kernel surface
+ *    at the caller's next synchronisation, as for any HIP kernel.
+ *  - Per (batch, head) slice, N * D * 2 bytes must stay below 2 GiB (the
+ *    kernels address one slice with 32-bit offsets); larger slices return
+ *    FA_ERR_TOO_LARGE.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same definition as the HIP runtime's, so this header needs no HIP include. */
+typedef struct ihipStream_t* hipStream_t;
+
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    FA_ERR_SHAPE = 2,       /* B, H, N, nseq, total or max_seqlen out of range */
+    FA_ERR_UNSUPPORTED = 3, /* D not in {64, 128}, or causal not in {0, 1}     */
+    FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
+    FA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required         */
+    FA_ERR_LAUNCH = 6,      /* a kernel launch failed (HIP error)              */
+    FA_ERR_ARG = 7,         /* softmax_scale not finite or not > 0             */
+    FA_ERR_TOO_LARGE = 8    /* a (batch, head) slice exceeds 2 GiB             */
+};
+
+/*
+ * Forward pass, dense batch.
+ *
+ * Computes O = softmax(scale * Q K^T (masked)) V and the row log-sum-exp L
+ * with the query-first tiled schedule of tensortonic section 6: each work
+ * unit keeps one query tile on chip, streams the key/value tiles past it,
+ * keeps a running maximum m, denominator l and unnormalised accumulator u per
+ * query row (section 5), rescales by exp(m_old - m_new) when the maximum
+ * grows, and writes O = u / l and L = m + ln l once at the end.  Under causal
+ * masking, key tiles wholly in the future are skipped and the element mask is
+ * applied only on tiles that cross the diagonal (section 6).
+ *
+ *   q, k, v   in   bf16 [B, H, N, D]
+ *   o         out  bf16 [B, H, N, D]   (fully overwritten)
+ *   lse       out  fp32 [B, H, N]      (may be NULL when not needed)
+ *   B, H, N   >= 1;  D in {64, 128};  causal in {0, 1}
+ *
+ * Returns FA_OK or an fa_status code.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int D, float softmax_scale, int causal,
+           hipStream_t stream);
+
+/*
+ * Forward pass over packed variable-length sequences (nexusofnerds
+ * "FlashAttention": variable-length packing; padding would otherwise waste
+ * work).  nseq sequences are concatenated along the token axis; sequence b
+ * owns packed tokens [cu_seqlens[b], cu_seqlens[b+1]).  Each sequence attends
+ * only to itself, with causal positions relative to its own start.
+ *
+ *   q, k, v     in   bf16 [H, total, D]
+ *   o           out  bf16 [H, total, D]  (rows of every sequence overwritten)
+ *   lse         out  fp32 [H, total]     (may be NULL)
+ *   cu_seqlens  in   DEVICE int32 [nseq + 1]: cu[0] = 0, non-decreasing,
+ *                    cu[nseq] = total.  Zero-length sequences are allowed.
+ *   max_seqlen  host int >= every sequence length (sizes the launch grid so
+ *                    no device-to-host copy is needed).  Rows of a sequence
+ *                    longer than max_seqlen are not written.
+ *   nseq, total, max_seqlen, H >= 1;  D in {64, 128}
+ *
+ * The offsets cannot be checked on the host; the kernels clamp them to
+ * [0, total] so malformed offsets never cause out-of-range accesses (their
+ * results are then unspecified).
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                  float* lse, const int32_t* cu_seqlens, int nseq, int total,
+                  int max_seqlen, int H, int D, float softmax_scale,
+                  int causal, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes (0 if the sizes
+ * are invalid).  The workspace holds one float32 per query row
+ * (D_i = <dO_i, O_i>), padded to 256 bytes.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int D);
+
+/*
+ * Backward pass, dense batch (tensortonic section 7): reloads query and key
+ * tiles, recomputes each score tile, rebuilds its weights as
+ * exp(s_ij - L_i) from the saved row log-sum-exp, and accumulates the
+ * gradients of sum(dout * O) with respect to q, k and v; the N x N weights
+ * are never stored.  There is no dropout.
+ *
+ *   q, k, v, o, dout   in   bf16 [B, H, N, D]; o and lse must come from
+ *                           fa_fwd on the same q, k, v, scale and causal
+ *   lse                in   fp32 [B, H, N]
+ *   dq, dk, dv         out  bf16 [B, H, N, D] (fully overwritten)
+ *   workspace          scratch device memory of at least
+ *                      fa_bwd_workspace_size(B, H, N, D) bytes; contents on
+ *                      entry are ignored, on exit unspecified
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+           void* workspace, size_t workspace_bytes, int B, int H, int N, int D,
+           float softmax_scale, int causal, hipStream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,127 @@
+"""C-ABI contract tests that need no GPU.
+
+The library must load, export every entry point include/fa.h declares, and
+reject every invalid argument with its documented status before any HIP call.
+Pointers passed here are never dereferenced: each call carries exactly one
+invalid argument, so validation returns before a launch could happen.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import exact_io_aware_44_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, LAUNCH, ARG, TOO_LARGE = range(9)
+P = 0x10000          # a 16-byte-aligned stand-in address, never dereferenced
+PM = 0x10008         # misaligned by 8 bytes
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.load()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert names == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd",
+                     "fa_fwd_varlen", "fa_status_string"]
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        s = fa.fa_status_string(code)
+        assert s.startswith("FA_"), s
+    assert "unknown" in fa.fa_status_string(99)
+    assert "unknown" in fa.fa_status_string(-1)
+    err = fa.FaError(UNSUP, "fa_fwd")
+    assert err.status == UNSUP and "FA_ERR_UNSUPPORTED" in str(err)
+
+
+def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=16, D=64, scale=0.125,
+        causal=0):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, D, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL),
+    (dict(o=None), NULL),
+    (dict(B=0), SHAPE), (dict(H=0), SHAPE), (dict(N=0), SHAPE),
+    (dict(N=-5), SHAPE), (dict(B=70000), SHAPE), (dict(H=70000), SHAPE),
+    (dict(D=96), UNSUP), (dict(D=256), UNSUP), (dict(D=0), UNSUP),
+    (dict(causal=2), UNSUP), (dict(causal=-1), UNSUP),
+    (dict(scale=0.0), ARG), (dict(scale=-0.1), ARG),
+    (dict(scale=float("nan")), ARG), (dict(scale=float("inf")), ARG),
+    (dict(q=PM), ALIGN), (dict(k=PM), ALIGN), (dict(v=PM), ALIGN),
+    (dict(o=PM), ALIGN), (dict(lse=P + 4), ALIGN),
+    (dict(N=1 << 23, D=128), TOO_LARGE), (dict(N=1 << 24, D=64), TOO_LARGE),
+])
+def test_fwd_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def varlen(lib, q=P, k=P, v=P, o=P, lse=P, cu=P, nseq=2, total=32, maxlen=16,
+           H=2, D=128, scale=0.1, causal=1):
+    return lib.fa_fwd_varlen(q, k, v, o, lse, cu, nseq, total, maxlen, H, D,
+                             scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), NULL), (dict(q=None), NULL), (dict(o=None), NULL),
+    (dict(nseq=0), SHAPE), (dict(total=0), SHAPE), (dict(maxlen=0), SHAPE),
+    (dict(H=0), SHAPE), (dict(nseq=70000), SHAPE),
+    (dict(D=32), UNSUP), (dict(causal=5), UNSUP), (dict(scale=-1.0), ARG),
+    (dict(cu=P + 2), ALIGN), (dict(v=PM), ALIGN),
+    (dict(total=1 << 23, D=128), TOO_LARGE),
+])
+def test_varlen_rejects(lib, kw, code):
+    assert varlen(lib, **kw) == code
+
+
+def test_workspace_size(lib):
+    assert fa.fa_bwd_workspace_size(2, 32, 4096, 128) == 2 * 32 * 4096 * 4
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 64) == 256  # padded to 256 bytes
+    assert fa.fa_bwd_workspace_size(0, 1, 3, 64) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 80) == 0
+
+
+def bwd(lib, q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, ws=P,
+        ws_bytes=1 << 20, B=1, H=2, N=64, D=128, scale=0.1, causal=1):
+    return lib.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, ws_bytes, B, H, N, D,
+                      scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(lse=None), NULL), (dict(do=None), NULL),
+    (dict(dq=None), NULL), (dict(dk=None), NULL), (dict(dv=None), NULL),
+    (dict(B=0), SHAPE), (dict(N=0), SHAPE), (dict(H=-1), SHAPE),
+    (dict(D=100), UNSUP), (dict(causal=7), UNSUP), (dict(scale=0.0), ARG),
+    (dict(dk=PM), ALIGN), (dict(lse=P + 4), ALIGN), (dict(ws=PM), ALIGN),
+    (dict(ws=None), WS), (dict(ws_bytes=100), WS),
+    (dict(N=1 << 24), TOO_LARGE),
+])
+def test_bwd_rejects(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def test_python_binding_checks_dtypes():
+    import torch
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(TypeError):
+        fa.fa_fwd(x, x, x)
+    y = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(y, y, y)  # CPU tensors are refused: no CPU fallback
