@@ -115,6 +115,31 @@ def cpu_baseline(budget_s: float):
     }
 
 
+def run_backward(torch, ai, fa, steps):
+    """fa_bwd on causal B2 H32 N4096 D128 (O and L from fa_fwd)."""
+    wb = ai.BACKWARD
+    log("backward", wb.name)
+    qb, kb, vb, dob = (x.cuda() for x in ai.backward_inputs())
+    ob, lseb = fa.fa_fwd(qb, kb, vb, softmax_scale=wb.scale, causal=True)
+    dq, dk, dv = (torch.empty_like(qb) for _ in range(3))
+    ws = torch.empty(fa.fa_bwd_workspace_size(wb.B, wb.H, wb.N, wb.D),
+                     dtype=torch.uint8, device="cuda")
+
+    def bwd_step():
+        fa.fa_bwd(qb, kb, vb, ob, lseb, dob, softmax_scale=wb.scale, causal=True,
+                  dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    btotal, bper = time_launches(torch, bwd_step, steps, 3)
+    bflops = 2.5 * fwd_flops(wb.B, wb.H, wb.N, wb.D, True)
+    b_ms = btotal / steps
+    backward = {"workload": wb.name, "ms": round(b_ms, 4),
+                "tflops": round(bflops / (b_ms * 1e-3) / 1e12, 2),
+                "frac": round(bflops / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "flops_per_call": bflops, "launches": 3}
+    del qb, kb, vb, dob, ob, lseb, dq, dk, dv, ws
+    return backward
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +148,9 @@ def main(argv=None):
     ap.add_argument("--bwd-steps", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain device-to-device copy of MIB MiB "
+                         "three times (reference for HBM byte counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -137,6 +165,16 @@ def main(argv=None):
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     fa.load()
+
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        log("copy calibration: %d bytes per copy" % nbytes)
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- forward: the metric -------------------------------------------------
     w = ai.CAUSAL
@@ -158,26 +196,11 @@ def main(argv=None):
     del q, k, v, o, lse
 
     # ---- backward against the same roofline ---------------------------------
-    wb = ai.BACKWARD
-    log("backward", wb.name)
-    qb, kb, vb, dob = (x.cuda() for x in ai.backward_inputs())
-    ob, lseb = fa.fa_fwd(qb, kb, vb, softmax_scale=wb.scale, causal=True)
-    dq, dk, dv = (torch.empty_like(qb) for _ in range(3))
-    ws = torch.empty(fa.fa_bwd_workspace_size(wb.B, wb.H, wb.N, wb.D),
-                     dtype=torch.uint8, device="cuda")
+    backward = None
+    if args.bwd_steps > 0:
+        backward = run_backward(torch, ai, fa, args.bwd_steps)
 
-    def bwd_step():
-        fa.fa_bwd(qb, kb, vb, ob, lseb, dob, softmax_scale=wb.scale, causal=True,
-                  dq=dq, dk=dk, dv=dv, workspace=ws)
 
-    btotal, bper = time_launches(torch, bwd_step, args.bwd_steps, 3)
-    bflops = 2.5 * fwd_flops(wb.B, wb.H, wb.N, wb.D, True)
-    b_ms = btotal / args.bwd_steps
-    backward = {"workload": wb.name, "ms": round(b_ms, 4),
-                "tflops": round(bflops / (b_ms * 1e-3) / 1e12, 2),
-                "frac": round(bflops / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "flops_per_call": bflops, "launches": 3}
-    del qb, kb, vb, dob, ob, lseb, dq, dk, dv, ws
 
     line = {
         "metric": METRIC,

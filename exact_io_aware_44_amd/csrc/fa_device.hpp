@@ -17,6 +17,8 @@
 //   bf16 matrix, lane l receives the column C + l%16 of rows R..R+3: a
 //   row-major tile becomes a column-major MFMA operand without a transposed
 //   copy in LDS.
+//
+//   buffer_load_dwordx4 ... lds: lane i writes its 16 bytes at M0 + 16*i.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -65,6 +67,18 @@ __device__ __forceinline__ void store8(Buf b, uint32_t off, u32x2 v) {
 __device__ __forceinline__ void store4(Buf b, uint32_t off, uint32_t v) {
     __builtin_amdgcn_raw_buffer_store_b32(v, b.r, off, 0, 0);
 }
+// Direct global -> LDS load (buffer_load_dwordx4 ... lds): lane i of the wave
+// writes its 16 bytes to lds_wave_base + 16*i (the base must be wave-uniform;
+// it goes to M0).  Out-of-range lanes write zeros and fetch nothing.
+__device__ __forceinline__ void load16_lds(Buf b, uint32_t off, void* lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (FA_LDS void*)lds_wave_base, 16, off,
+                                             0, 0, 0);
+}
+// Offset that is out of range for every buffer (all buffers are < 2 GiB).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+// s_waitcnt vmcnt(0) only (gfx9 encoding: expcnt and lgkmcnt left at max).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ float loadf(Buf b, uint32_t off) {
     return __builtin_bit_cast(float,
                               __builtin_amdgcn_raw_buffer_load_b32(b.r, off, 0, 0));

@@ -20,14 +20,19 @@
 //    O^T += V^T P^T (the key order inside an MFMA k-step is a free
 //    permutation, matched on the V side).  V stays row-major in LDS and is
 //    read with ds_read_b64_tr_b16, which delivers it column-major.
-//  - Exponentials use exp2 with scale*log2(e) folded into one FMA per score.
-//  - K/V tiles are double-buffered in LDS: the global loads of tile j+1 are
-//    issued before the MFMAs of tile j and written to the other buffer after,
-//    so one barrier per tile suffices.
+//  - Exponentials use exp2 with scale*log2(e) folded into one FMA per score;
+//    the running maximum moves lazily (see kLazyRescale), so the accumulator
+//    rescale is skipped on almost every tile.
+//  - K and V tiles have separate LDS double buffers with K one tile ahead:
+//    while the softmax of tile j runs on the VALU, S for tile j+1 is already
+//    computable on the MFMA unit from K_{j+1} in LDS.  Global loads for
+//    K_{j+2} and V_{j+1} are issued at the top of iteration j and written to
+//    the buffers no wave reads during it, so one barrier per tile suffices.
 //  - Causal: key tiles wholly after the unit's last row are never loaded; a
 //    wave skips tiles wholly after its own rows; the element mask runs only on
 //    tiles crossing the diagonal (or the ragged end of the sequence).
-//  - Units are launched heaviest first under causal masking.
+//  - A 1-D grid is remapped so that each XCD owns whole heads (their K/V
+//    re-reads hit its private L2), heaviest query tile first.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -39,14 +44,35 @@ struct FwdTile {
     static constexpr int BR = 128;       // query rows per work unit
     static constexpr int BC = 64;        // keys per streamed tile
     static constexpr int THREADS = 256;
-    static constexpr int KSTR = D + 8;   // K row pitch (elements): rows 4 banks apart
-    static constexpr int VSTR = D + 32;  // V row pitch: rows 16 banks apart
+    static constexpr int CPR = D / 8;    // 16-byte chunks per row
+    // K: row pitch padded by one chunk, so the 16 rows a quarter-wave reads
+    // with ds_read_b128 land 4 banks apart (conflict-free)
+    static constexpr int KSTR = D + 8;
+    static constexpr int KCH = KSTR / 8;               // chunks per padded row
+    static constexpr int K_LOADS = BC * KCH / 64;      // wave-wide 1 KiB loads
+    // V: unpadded rows, chunk index XOR-swizzled (see v_swz) so the transpose
+    // reads of four rows x 64 bytes per half-wave hit distinct banks
+    static constexpr int V_LOADS = BC * CPR / 64;
     static constexpr int K_ELEMS = BC * KSTR;
-    static constexpr int STAGE = BC * (KSTR + VSTR);
-    static constexpr int CPT = BC * D / 8 / THREADS;  // 16 B chunks / thread / tensor
+    static constexpr int V_ELEMS = BC * D;
+    static constexpr int LDS_ELEMS = 2 * K_ELEMS + 2 * V_ELEMS;  // K x2, V x2
     static constexpr int DS = D / 16;    // MFMA k-steps across the head width
     static constexpr int DB = D / 32;    // 32-wide blocks of the output
+    static constexpr int RPL = 64 / CPR; // V rows per wave-wide load
 };
+
+// XOR applied to the 16-byte chunk index of V row r in LDS.
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+    return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+// The running maximum only moves when a tile exceeds it by more than this
+// many base-2 units; until then new weights are taken against the stale
+// maximum (so they are at most 2^8) and the accumulators need no rescale.
+// Every weight and both sums still share one reference point, so O = u / l
+// and L = m + ln l are unchanged up to rounding.
+constexpr float kLazyRescale = 8.f;
 
 struct FwdParams {
     const bf16* q;
@@ -61,15 +87,29 @@ struct FwdParams {
     float c;   // softmax_scale * log2(e)
 };
 
+// Unit schedule.  Workgroup i of a 1-D grid is dispatched to XCD i % 8; the
+// remap below gives each XCD a contiguous range of units, head-major and
+// heaviest query tile first, so the K/V re-reads of one head stay in that
+// XCD's L2 and the light units of the causal triangle run last.
+__device__ __forceinline__ void unit_of(int i, int total, int n_qt, bool causal,
+                                        int& head, int& qt) {
+    const int L = (total & 7) == 0 ? (i & 7) * (total >> 3) + (i >> 3) : i;
+    head = L / n_qt;
+    const int r = L - head * n_qt;
+    qt = causal ? n_qt - 1 - r : r;
+}
+
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     using T = FwdTile<D>;
-    __shared__ __attribute__((aligned(16))) bf16 lds[2 * T::STAGE];
+    __shared__ __attribute__((aligned(16))) bf16 lds[T::LDS_ELEMS];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
-    const int qt = CAUSAL ? (p.n_qt - 1 - (int)blockIdx.x) : (int)blockIdx.x;
-    const int h = blockIdx.y, b = blockIdx.z;
+    const int g = lane >> 4, i16 = lane & 15;
+    int head, qt;
+    unit_of(blockIdx.x, gridDim.x, p.n_qt, CAUSAL, head, qt);
+    const int b = head / p.H, h = head - b * p.H;
 
     int n;
     int64_t row0;
@@ -112,51 +152,60 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     for (int e = 0; e < T::DB; ++e) acc[e] = f32x16{};
     float m_run = kNegInf, l_run = 0.f;  // l_run: this lane's half of the keys
 
-    u32x4 kreg[T::CPT], vreg[T::CPT];
-    auto gload = [&](int k0) {
+    // ---- tile movement: global -> LDS directly (no staging registers).
+    //      Wave w issues the wave-wide 1 KiB loads w, w+4, ...; each lane's
+    //      byte offset inside a tile is fixed, only the tile origin moves. ----
+    constexpr int KL = (T::K_LOADS + 3) / 4, VL = (T::V_LOADS + 3) / 4;
+    uint32_t koff[KL];
 #pragma unroll
-        for (int i = 0; i < T::CPT; ++i) {
-            const int c = tid + T::THREADS * i;
-            const int r = c / (D / 8), cc = c % (D / 8);
-            const uint32_t off = ((uint32_t)(k0 + r) * D + cc * 8) * 2;
-            kreg[i] = load16(kb, off);
-            vreg[i] = load16(vb, off);
+    for (int x = 0; x < KL; ++x) {
+        const int t = wave + 4 * x;
+        const int P = 64 * t + lane;  // padded chunk slot written by this lane
+        const int r = P / T::KCH, c = P % T::KCH;
+        koff[x] = (t < T::K_LOADS && c < T::CPR) ? (uint32_t)(r * D + c * 8) * 2
+                                                  : kOutOfRange;  // pad: no fetch
+    }
+    // V: lane writes row RPL*t + lane/CPR, physical chunk lane%CPR, which holds
+    // logical chunk (lane%CPR) ^ v_swz(row); v_swz depends on lane only here.
+    const uint32_t voff = (uint32_t)((lane / T::CPR) * D +
+                                     (((lane % T::CPR) ^ v_swz<D>(lane / T::CPR)) * 8)) * 2;
+    auto load_k = [&](int k0, bf16* dst) {
+#pragma unroll
+        for (int x = 0; x < KL; ++x) {
+            const int t = wave + 4 * x;
+            if (t < T::K_LOADS)
+                load16_lds(kb, koff[x] + (uint32_t)k0 * D * 2, dst + 512 * t);
         }
     };
-    auto lstore = [&](int stage) {
-        bf16* ks = lds + stage * T::STAGE;
-        bf16* vs = ks + T::K_ELEMS;
+    auto load_v = [&](int k0, bf16* dst) {
 #pragma unroll
-        for (int i = 0; i < T::CPT; ++i) {
-            const int c = tid + T::THREADS * i;
-            const int r = c / (D / 8), cc = c % (D / 8);
-            lds_write16(ks + r * T::KSTR + cc * 8, kreg[i]);
-            lds_write16(vs + r * T::VSTR + cc * 8, vreg[i]);
+        for (int x = 0; x < VL; ++x) {
+            const int t = wave + 4 * x;
+            if (t < T::V_LOADS)
+                load16_lds(vb, voff + (uint32_t)(k0 + T::RPL * t) * D * 2, dst + 512 * t);
         }
     };
+    auto kbuf = [&](int i) { return lds + (i & 1) * T::K_ELEMS; };
+    auto vbuf = [&](int i) { return lds + 2 * T::K_ELEMS + (i & 1) * T::V_ELEMS; };
 
-    const int g = lane >> 4, i16 = lane & 15;
-    auto compute = [&](int stage, int k0) {
-        if (CAUSAL && k0 > qw0 + 31) return;  // tile wholly in this wave's future
-        const bf16* ks = lds + stage * T::STAGE;
-        const bf16* vs = ks + T::K_ELEMS;
-
-        // S^T for two 32-key blocks: lane holds query qi, keys
-        // k0 + 32*bb + 8*(r/4) + 4*hi + r%4.
-        f32x16 s[2];
+    // ---- S^T = K Q^T for one tile: lane holds query qi and keys
+    //      k0 + 32*bb + 8*(r/4) + 4*hi + r%4 ---------------------------------
+    auto scores = [&](const bf16* ks, f32x16* s) {
+        s[0] = f32x16{};
+        s[1] = f32x16{};
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            s[bb] = f32x16{};
+        for (int ss = 0; ss < T::DS; ++ss)
 #pragma unroll
-            for (int ss = 0; ss < T::DS; ++ss)
+            for (int bb = 0; bb < 2; ++bb)
                 s[bb] = mfma32(
                     lds_read16(ks + (32 * bb + l32) * T::KSTR + 16 * ss + 8 * hi),
                     qreg[ss], s[bb]);
-        }
+    };
+
+    // ---- online softmax of one score tile, then O^T += V^T P^T ------------
+    auto softmax_pv = [&](f32x16* s, const bf16* vs, int k0) {
         // element mask only on tiles crossing the diagonal or the sequence end
-        const bool need_mask =
-            (CAUSAL && k0 + T::BC - 1 > qw0) || (k0 + T::BC > n);
-        if (need_mask) {
+        if ((CAUSAL && k0 + T::BC - 1 > qw0) || k0 + T::BC > n) {
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
@@ -165,64 +214,80 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
                     if ((CAUSAL && key > qi) || key >= n) s[bb][r] = kNegInf;
                 }
         }
-        // running maximum (scaled, base-2 units)
         float mx = kNegInf;
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bb][r]);
-        mx = fmaxf(mx, xor32(mx));
-        const float m_new = fmaxf(m_run, mx * p.c);
+        mx = fmaxf(mx, xor32(mx)) * p.c;  // tile row maximum, base-2 units
+        const bool upd = mx > m_run + kLazyRescale;  // first live tile: always
+        const float m_new = upd ? mx : m_run;
         const float m_use = (m_new == kNegInf) ? 0.f : m_new;  // no key yet: no NaN
-        const float alpha = exp2_fast(m_run - m_use);
+        const float alpha = upd ? exp2_fast(m_run - m_use) : 1.f;
+        if (__any(upd)) {
+#pragma unroll
+            for (int e = 0; e < T::DB; ++e) acc[e] *= alpha;
+        }
+        m_run = m_new;
         float rs = 0.f;
+        bf16x8 pb[2][2];
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float e = exp2_fast(__builtin_fmaf(s[bb][r], p.c, -m_use));
-                s[bb][r] = e;
                 rs += e;
+                pb[bb][r >> 3][r & 7] = to_bf16(e);
             }
         l_run = __builtin_fmaf(l_run, alpha, rs);
-#pragma unroll
-        for (int e = 0; e < T::DB; ++e) acc[e] *= alpha;
-        m_run = m_new;
-
-        // P^T as bf16 B operands: k-step t of block bb = registers 8t..8t+7
-        bf16x8 pb[2][2];
+        // O^T += V^T P^T; V^T delivered by transpose reads of row-major V.
+        // Rows kr, kr+8 (kr = 32bb + 16t + 4hi + i16/4) share v_swz(kr), so
+        // the swizzled column offset depends on the lane and e only.
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t) {
+                const int kr = 32 * bb + 16 * t + 4 * hi + (i16 >> 2);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) pb[bb][t][j] = to_bf16(s[bb][8 * t + j]);
-
-        // O^T += V^T P^T, V^T delivered by transpose reads of row-major V
-#pragma unroll
-        for (int e = 0; e < T::DB; ++e) {
-            const int dcol = 32 * e + 16 * (g & 1) + 4 * (i16 & 3);
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int kr = 32 * bb + 16 * t + 4 * hi + (i16 >> 2);
-                    const bf16x4 va = lds_read_tr(vs + kr * T::VSTR + dcol);
-                    const bf16x4 vc = lds_read_tr(vs + (kr + 8) * T::VSTR + dcol);
+                for (int e = 0; e < T::DB; ++e) {
+                    const int dcol = 32 * e + 16 * (g & 1) + 4 * (i16 & 3);
+                    const int col = (((dcol >> 3) ^ v_swz<D>(kr)) << 3) + (dcol & 7);
+                    const bf16x4 va = lds_read_tr(vs + kr * D + col);
+                    const bf16x4 vc = lds_read_tr(vs + (kr + 8) * D + col);
                     acc[e] = mfma32(cat(va, vc), pb[bb][t], acc[e]);
                 }
-        }
+            }
     };
 
-    gload(0);
-    lstore(0);
+    // ---- software pipeline: during tile j, K_{j+1} is already in LDS, so
+    //      S_{j+1} = K_{j+1} Q^T (MFMA) and the softmax of S_j (VALU) are
+    //      independent; K_{j+2} and V_{j+1} load into the buffers no wave
+    //      reads this iteration, so one barrier per tile suffices. -----------
+    load_k(0, kbuf(0));
+    load_v(0, vbuf(0));
+    if (nkt > 1) load_k(T::BC, kbuf(1));
+    __builtin_amdgcn_s_waitcnt(0);  // Q registers and the first tiles landed
     __syncthreads();
-    for (int kt = 0; kt < nkt; ++kt) {
-        const bool more = kt + 1 < nkt;
-        if (more) gload((kt + 1) * T::BC);
-        compute(kt & 1, kt * T::BC);
-        if (more) lstore((kt + 1) & 1);
+
+    f32x16 s_cur[2], s_nxt[2];
+    scores(kbuf(0), s_cur);  // tile 0 is never in any wave's future
+    for (int j = 0; j < nkt; ++j) {
+        const int k0 = j * T::BC;
+        const bool more1 = j + 1 < nkt, more2 = j + 2 < nkt;
+        if (more2) load_k(k0 + 2 * T::BC, kbuf(j));      // K_j was consumed last iteration
+        if (more1) load_v(k0 + T::BC, vbuf(j + 1));      // V_{j-1} likewise
+        const bool live = !(CAUSAL && k0 > qw0 + 31);    // tile j not wholly in future
+        const bool live_nxt = more1 && !(CAUSAL && k0 + T::BC > qw0 + 31);
+        if (live_nxt) {
+            scores(kbuf(j + 1), s_nxt);
+            softmax_pv(s_cur, vbuf(j), k0);
+        } else if (live) {
+            softmax_pv(s_cur, vbuf(j), k0);
+        }
+        wait_vmem();  // this iteration's tile loads have landed in LDS
         __syncthreads();
+        s_cur[0] = s_nxt[0];
+        s_cur[1] = s_nxt[1];
     }
 
     // epilogue: O = u / l (bf16), L = m + ln l (natural log, scaled units)
@@ -257,9 +322,9 @@ hipError_t run_fwd(const FwdArgs& a, hipStream_t stream) {
     p.N = a.N;
     p.n_qt = (a.max_seqlen + T::BR - 1) / T::BR;
     p.c = (float)((double)a.scale * 1.4426950408889634);
-    const dim3 grid(p.n_qt, a.H, a.B);
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, VARLEN>), grid, dim3(T::THREADS), 0,
-                       stream, p);
+    const int64_t units = (int64_t)p.n_qt * a.H * a.B;
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)units),
+                       dim3(T::THREADS), 0, stream, p);
     return hipGetLastError();
 }
 
