@@ -104,7 +104,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     using T = FwdTile<D>;
     __shared__ __attribute__((aligned(16))) bf16 lds[T::LDS_ELEMS];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int l32 = lane & 31, hi = lane >> 5;
     const int g = lane >> 4, i16 = lane & 15;
     int head, qt;
@@ -202,35 +203,38 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
                     qreg[ss], s[bb]);
     };
 
-    // ---- online softmax of one score tile, then O^T += V^T P^T ------------
-    auto softmax_pv = [&](f32x16* s, const bf16* vs, int k0) {
-        // element mask only on tiles crossing the diagonal or the sequence end
-        if ((CAUSAL && k0 + T::BC - 1 > qw0) || k0 + T::BC > n) {
+    // ---- element mask: only on tiles crossing the diagonal or the sequence
+    //      end.  Element (bb, r) is key k0 + 32bb + 8(r/4) + 4hi + r%4; it is
+    //      allowed while that offset stays below this lane's limit. ----------
+    auto needs_mask = [&](int k0) {
+        return (CAUSAL && k0 + T::BC - 1 > qw0) || k0 + T::BC > n;
+    };
+    auto apply_mask = [&](f32x16* s, int k0) {
+        int lim = n - k0;                             // keys before the end
+        if (CAUSAL) lim = min(lim, qi - k0 + 1);      // keys j <= qi
+        lim -= 4 * hi;
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
+        for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * bb + 8 * (r / 4) + 4 * hi + (r & 3);
-                    if ((CAUSAL && key > qi) || key >= n) s[bb][r] = kNegInf;
-                }
-        }
+            for (int r = 0; r < 16; ++r)
+                if (32 * bb + 8 * (r / 4) + (r & 3) >= lim) s[bb][r] = kNegInf;
+    };
+
+    // ---- online softmax statistics of one score tile: new running maximum
+    //      (lazy), rescale factor, exponentials as bf16 B operands, row sum --
+    auto softmax = [&](f32x16* s, bf16x8 (&pb)[2][2], float& alpha, bool& upd) {
         float mx = kNegInf;
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bb][r]);
         mx = fmaxf(mx, xor32(mx)) * p.c;  // tile row maximum, base-2 units
-        const bool upd = mx > m_run + kLazyRescale;  // first live tile: always
+        upd = mx > m_run + kLazyRescale;  // the first live tile always moves it
         const float m_new = upd ? mx : m_run;
         const float m_use = (m_new == kNegInf) ? 0.f : m_new;  // no key yet: no NaN
-        const float alpha = upd ? exp2_fast(m_run - m_use) : 1.f;
-        if (__any(upd)) {
-#pragma unroll
-            for (int e = 0; e < T::DB; ++e) acc[e] *= alpha;
-        }
+        alpha = upd ? exp2_fast(m_run - m_use) : 1.f;
         m_run = m_new;
         float rs = 0.f;
-        bf16x8 pb[2][2];
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
@@ -240,9 +244,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
                 pb[bb][r >> 3][r & 7] = to_bf16(e);
             }
         l_run = __builtin_fmaf(l_run, alpha, rs);
-        // O^T += V^T P^T; V^T delivered by transpose reads of row-major V.
-        // Rows kr, kr+8 (kr = 32bb + 16t + 4hi + i16/4) share v_swz(kr), so
-        // the swizzled column offset depends on the lane and e only.
+    };
+
+    // ---- O^T += V^T P^T; V^T delivered by transpose reads of row-major V.
+    //      Rows kr, kr+8 (kr = 32bb + 16t + 4hi + i16/4) share v_swz(kr), so
+    //      the swizzled column depends on the lane and e only. ---------------
+    auto pv = [&](const bf16x8 (&pb)[2][2], const bf16* vs) {
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
@@ -258,11 +265,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
                 }
             }
     };
+    auto rescale = [&](float alpha, bool upd) {
+        if (__any(upd)) {
+#pragma unroll
+            for (int e = 0; e < T::DB; ++e) acc[e] *= alpha;
+        }
+    };
 
     // ---- software pipeline: during tile j, K_{j+1} is already in LDS, so
-    //      S_{j+1} = K_{j+1} Q^T (MFMA) and the softmax of S_j (VALU) are
-    //      independent; K_{j+2} and V_{j+1} load into the buffers no wave
-    //      reads this iteration, so one barrier per tile suffices. -----------
+    //      S_{j+1} = K_{j+1} Q^T (MFMA) and the softmax of S_j (VALU) form one
+    //      branch-free block the scheduler can interleave.  K_{j+2} and V_{j+1}
+    //      load into the buffers no wave reads this iteration, so one barrier
+    //      per tile suffices.  The last tile is peeled off the loop. ---------
     load_k(0, kbuf(0));
     load_v(0, vbuf(0));
     if (nkt > 1) load_k(T::BC, kbuf(1));
@@ -271,23 +285,37 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 
     f32x16 s_cur[2], s_nxt[2];
     scores(kbuf(0), s_cur);  // tile 0 is never in any wave's future
-    for (int j = 0; j < nkt; ++j) {
+    for (int j = 0; j + 1 < nkt; ++j) {
         const int k0 = j * T::BC;
-        const bool more1 = j + 1 < nkt, more2 = j + 2 < nkt;
-        if (more2) load_k(k0 + 2 * T::BC, kbuf(j));      // K_j was consumed last iteration
-        if (more1) load_v(k0 + T::BC, vbuf(j + 1));      // V_{j-1} likewise
-        const bool live = !(CAUSAL && k0 > qw0 + 31);    // tile j not wholly in future
-        const bool live_nxt = more1 && !(CAUSAL && k0 + T::BC > qw0 + 31);
-        if (live_nxt) {
+        if (j + 2 < nkt) load_k(k0 + 2 * T::BC, kbuf(j));  // K_j consumed last iteration
+        load_v(k0 + T::BC, vbuf(j + 1));                    // V_{j-1} likewise
+        // a wave whose rows all precede tile j is done (its later tiles too)
+        if (!(CAUSAL && k0 > qw0 + 31)) {
+            if (needs_mask(k0)) apply_mask(s_cur, k0);
+            bf16x8 pb[2][2];
+            float alpha;
+            bool upd;
             scores(kbuf(j + 1), s_nxt);
-            softmax_pv(s_cur, vbuf(j), k0);
-        } else if (live) {
-            softmax_pv(s_cur, vbuf(j), k0);
+            softmax(s_cur, pb, alpha, upd);
+            rescale(alpha, upd);
+            pv(pb, vbuf(j));
+            s_cur[0] = s_nxt[0];
+            s_cur[1] = s_nxt[1];
         }
         wait_vmem();  // this iteration's tile loads have landed in LDS
         __syncthreads();
-        s_cur[0] = s_nxt[0];
-        s_cur[1] = s_nxt[1];
+    }
+    {
+        const int j = nkt - 1, k0 = j * T::BC;
+        if (!(CAUSAL && k0 > qw0 + 31)) {
+            if (needs_mask(k0)) apply_mask(s_cur, k0);
+            bf16x8 pb[2][2];
+            float alpha;
+            bool upd;
+            softmax(s_cur, pb, alpha, upd);
+            rescale(alpha, upd);
+            pv(pb, vbuf(j));
+        }
     }
 
     // epilogue: O = u / l (bf16), L = m + ln l (natural log, scaled units)
