@@ -1,7 +1,7 @@
 // fa_api.cpp -- the C ABI declared in include/fa.h: argument validation
 // (completed before any HIP call, so every rejection is side-effect free and
 // testable without a GPU), then dispatch to the kernel launchers.
-#include "../../include/fa.h"
+#include "fa.h"
 
 #include <hip/hip_runtime.h>
 
