@@ -115,6 +115,23 @@ __device__ __forceinline__ float log2_fast(float x) {
 __device__ __forceinline__ float xor32(float x) {  // value of lane l ^ 32
     return __shfl_xor(x, 32, 64);
 }
+// v_permlane32_swap with both operands x: each lane ends up holding its own
+// value and that of lane l ^ 32 (in some order), so max/sum of the pair is a
+// pair reduction across the two halves of the wave without an LDS round trip.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x),
+                                                    false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]),
+                 __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x),
+                                                    false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
 __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
     bf16x4 v{to_bf16(a), to_bf16(b), to_bf16(c), to_bf16(d)};
     return __builtin_bit_cast(u32x2, v);

@@ -10,29 +10,40 @@
 // stored.
 //
 // Mapping to CDNA4:
-//  - 256 threads = 4 wave64s, each owning 32 query rows (BR = 128).
+//  - 256 threads = 4 wave64s; wave w owns the 32 query rows q0 + 4i + w of the
+//    128-row tile.  Spreading the rows makes every wave's causal range of key
+//    tiles identical, so the loop has no per-wave branches.
 //  - Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16
 //    with K read from LDS and Q held in registers.  In that orientation each
-//    lane holds ONE query row (lane % 32) and 16 of the 32 keys of a block,
-//    so the row maximum and sum are in-lane reductions plus one exchange with
-//    lane ^ 32, and the rescale factor is a per-lane scalar.
+//    lane holds ONE query row (lane % 32) and 16 of the 32 keys of a block, so
+//    the row maximum and sum are in-lane reductions plus one exchange with
+//    lane ^ 32 (v_permlane32_swap), and the rescale factor is a per-lane
+//    scalar.
 //  - The same registers, rounded to bf16, are already the B operand of
 //    O^T += V^T P^T (the key order inside an MFMA k-step is a free
 //    permutation, matched on the V side).  V stays row-major in LDS and is
 //    read with ds_read_b64_tr_b16, which delivers it column-major.
+//  - Software pipeline on 32-key half tiles: half-step h issues, in one
+//    branch-free block, the MFMAs of S_{h+1} = K_{h+1} Q^T and of
+//    O^T += V_{h-1}^T P_{h-1}^T together with the VALU softmax of S_h.  The
+//    three are independent, so the wave keeps the matrix pipe busy while its
+//    own exponentials run; every MFMA operand is requested from LDS four
+//    MFMAs ahead.  Two workgroups per CU give each SIMD a second such wave.
 //  - Exponentials use exp2 with scale*log2(e) folded into one FMA per score;
 //    the running maximum moves lazily (see kLazyRescale), so the accumulator
 //    rescale is skipped on almost every tile.
-//  - K and V tiles have separate LDS double buffers with K one tile ahead:
-//    while the softmax of tile j runs on the VALU, S for tile j+1 is already
-//    computable on the MFMA unit from K_{j+1} in LDS.  Global loads for
-//    K_{j+2} and V_{j+1} are issued at the top of iteration j and written to
-//    the buffers no wave reads during it, so one barrier per tile suffices.
-//  - Causal: key tiles wholly after the unit's last row are never loaded; a
-//    wave skips tiles wholly after its own rows; the element mask runs only on
-//    tiles crossing the diagonal (or the ragged end of the sequence).
+//  - Tiles (64 keys) move global -> LDS directly (buffer_load ... lds),
+//    double-buffered; the two half-steps of tile-step j read only K tile j+1
+//    and V tile j, so K_{j+2} and V_{j+1} load into the other buffers meanwhile
+//    and one barrier per tile suffices.
+//  - Causal: key tiles wholly after the unit's last row are never loaded; the
+//    element mask runs only on tiles crossing the diagonal (or the ragged end
+//    of the sequence); a unit processes a light and a heavy query tile of the
+//    same head so all units carry equal work.
 //  - A 1-D grid is remapped so that each XCD owns whole heads (their K/V
-//    re-reads hit its private L2), heaviest query tile first.
+//    re-reads hit its private L2).
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -41,24 +52,28 @@ namespace {
 
 template <int D>
 struct FwdTile {
-    static constexpr int BR = 128;       // query rows per work unit
-    static constexpr int BC = 64;        // keys per streamed tile
-    static constexpr int THREADS = 256;
-    static constexpr int CPR = D / 8;    // 16-byte chunks per row
+    static constexpr int WAVES = 4;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int BR = 32 * WAVES;  // query rows per tile
+    static constexpr int BC = 64;          // keys per streamed tile
+    static constexpr int CPR = D / 8;      // 16-byte chunks per row
     // K: row pitch padded by one chunk, so the 16 rows a quarter-wave reads
     // with ds_read_b128 land 4 banks apart (conflict-free)
     static constexpr int KSTR = D + 8;
-    static constexpr int KCH = KSTR / 8;               // chunks per padded row
-    static constexpr int K_LOADS = BC * KCH / 64;      // wave-wide 1 KiB loads
+    static constexpr int KCH = KSTR / 8;           // chunks per padded row
+    // wave-wide 1 KiB loads per K tile, rounded up to a multiple of the four
+    // waves so every wave issues the same count with no guard; the extra
+    // loads are out of range (no fetch) and only zero-fill the buffer's tail
+    static constexpr int K_LOADS = (BC * KCH / 64 + 3) / 4 * 4;
     // V: unpadded rows, chunk index XOR-swizzled (see v_swz) so the transpose
     // reads of four rows x 64 bytes per half-wave hit distinct banks
     static constexpr int V_LOADS = BC * CPR / 64;
-    static constexpr int K_ELEMS = BC * KSTR;
+    static constexpr int K_ELEMS = K_LOADS * 512;  // >= BC * KSTR
     static constexpr int V_ELEMS = BC * D;
     static constexpr int LDS_ELEMS = 2 * K_ELEMS + 2 * V_ELEMS;  // K x2, V x2
-    static constexpr int DS = D / 16;    // MFMA k-steps across the head width
-    static constexpr int DB = D / 32;    // 32-wide blocks of the output
-    static constexpr int RPL = 64 / CPR; // V rows per wave-wide load
+    static constexpr int DS = D / 16;      // MFMA k-steps across the head width
+    static constexpr int DB = D / 32;      // 32-wide blocks of the output
+    static constexpr int RPL = 64 / CPR;   // V rows per wave-wide load
 };
 
 // XOR applied to the 16-byte chunk index of V row r in LDS.
@@ -82,22 +97,23 @@ struct FwdParams {
     float* lse;
     const int32_t* cu;
     int H;
-    int N;     // tokens per sequence (dense) or packed total (varlen)
-    int n_qt;  // query tiles per (batch, head) in the grid
-    float c;   // softmax_scale * log2(e)
+    int N;         // tokens per sequence (dense) or packed total (varlen)
+    int per_head;  // units per (batch, head): query tiles, or pairs if causal
+    float c;       // softmax_scale * log2(e)
 };
 
 // Unit schedule.  Workgroup i of a 1-D grid is dispatched to XCD i % 8; the
-// remap below gives each XCD a contiguous range of units, head-major and
-// heaviest query tile first, so the K/V re-reads of one head stay in that
-// XCD's L2 and the light units of the causal triangle run last.
-__device__ __forceinline__ void unit_of(int i, int total, int n_qt, bool causal,
-                                        int& head, int& qt) {
+// remap below gives each XCD a contiguous range of units, head-major, so the
+// K/V re-reads of one head stay in that XCD's L2.
+__device__ __forceinline__ void unit_of(int i, int total, int per_head, int& head,
+                                        int& idx) {
     const int L = (total & 7) == 0 ? (i & 7) * (total >> 3) + (i >> 3) : i;
-    head = L / n_qt;
-    const int r = L - head * n_qt;
-    qt = causal ? n_qt - 1 - r : r;
+    head = L / per_head;
+    idx = L - head * per_head;
 }
+
+using True = std::true_type;
+using False = std::false_type;
 
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
@@ -108,8 +124,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int l32 = lane & 31, hi = lane >> 5;
     const int g = lane >> 4, i16 = lane & 15;
-    int head, qt;
-    unit_of(blockIdx.x, gridDim.x, p.n_qt, CAUSAL, head, qt);
+    int head, uidx;
+    unit_of(blockIdx.x, gridDim.x, p.per_head, head, uidx);
     const int b = head / p.H, h = head - b * p.H;
 
     int n;
@@ -124,8 +140,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         n = p.N;
         row0 = ((int64_t)b * p.H + h) * p.N;
     }
-    const int q0 = qt * T::BR;
-    if (q0 >= n) return;  // whole unit past the end of its sequence
+    // the query tiles of this unit, heavy first; ntiles is workgroup-uniform
+    const int n_tiles = (n + T::BR - 1) / T::BR;
+    int tile0 = uidx, tile1 = -1;
+    if (CAUSAL) {
+        tile0 = n_tiles - 1 - uidx;
+        tile1 = uidx;
+        if (tile1 > tile0) return;  // past the middle of this sequence's tiles
+        if (tile1 == tile0) tile1 = -1;
+    } else if (tile0 >= n_tiles) {
+        return;  // whole unit past the end of its sequence
+    }
+    const int ntiles = tile1 >= 0 ? 2 : 1;
 
     const uint32_t bytes = (uint32_t)n * D * 2;
     const Buf qb = make_buf(p.q + row0 * D, bytes);
@@ -135,8 +161,42 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     const Buf lb = p.lse ? make_buf(p.lse + row0, (uint32_t)n * 4)
                          : make_buf(nullptr, 0);
 
-    const int qw0 = q0 + 32 * wave;  // first query row of this wave
-    const int qi = qw0 + l32;        // query row held by this lane
+    // ---- tile movement: global -> LDS directly (no staging registers).
+    //      Wave w issues the wave-wide 1 KiB loads w, w+4, ...; each lane's
+    //      byte offset inside a tile is fixed, only the tile origin moves. ----
+    constexpr int KL = (T::K_LOADS + 3) / 4, VL = (T::V_LOADS + 3) / 4;
+    uint32_t koff[KL];
+#pragma unroll
+    for (int x = 0; x < KL; ++x) {
+        const int t = wave + 4 * x;
+        const int P = 64 * t + lane;  // padded chunk slot written by this lane
+        const int r = P / T::KCH, c = P % T::KCH;
+        koff[x] = (r < T::BC && c < T::CPR) ? (uint32_t)(r * D + c * 8) * 2
+                                             : kOutOfRange;  // pad: no fetch
+    }
+    // V: lane writes row RPL*t + lane/CPR, physical chunk lane%CPR, which holds
+    // logical chunk (lane%CPR) ^ v_swz(row); v_swz depends on lane only here.
+    const uint32_t voff = (uint32_t)((lane / T::CPR) * D +
+                                     (((lane % T::CPR) ^ v_swz<D>(lane / T::CPR)) * 8)) * 2;
+    static_assert(T::K_LOADS % 4 == 0 && T::V_LOADS % 4 == 0, "loads split evenly");
+    auto load_k = [&](int k0, bf16* dst) {
+#pragma unroll
+        for (int x = 0; x < KL; ++x)
+            load16_lds(kb, koff[x] + (uint32_t)k0 * D * 2, dst + 512 * (wave + 4 * x));
+    };
+    auto load_v = [&](int k0, bf16* dst) {
+#pragma unroll
+        for (int x = 0; x < VL; ++x) {
+            const int t = wave + 4 * x;
+            load16_lds(vb, voff + (uint32_t)(k0 + T::RPL * t) * D * 2, dst + 512 * t);
+        }
+    };
+    auto kbuf = [&](int i) { return lds + (i & 1) * T::K_ELEMS; };
+    auto vbuf = [&](int i) { return lds + 2 * T::K_ELEMS + (i & 1) * T::V_ELEMS; };
+
+    for (int rep = 0; rep < ntiles; ++rep) {
+    const int q0 = (rep == 0 ? tile0 : tile1) * T::BR;
+    const int qi = q0 + 4 * l32 + wave;  // query row held by this lane
 
     // Q as the B operand of S^T = K Q^T: lane holds Q[qi][16s + 8hi + 0..7].
     bf16x8 qreg[T::DS];
@@ -153,117 +213,52 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     for (int e = 0; e < T::DB; ++e) acc[e] = f32x16{};
     float m_run = kNegInf, l_run = 0.f;  // l_run: this lane's half of the keys
 
-    // ---- tile movement: global -> LDS directly (no staging registers).
-    //      Wave w issues the wave-wide 1 KiB loads w, w+4, ...; each lane's
-    //      byte offset inside a tile is fixed, only the tile origin moves. ----
-    constexpr int KL = (T::K_LOADS + 3) / 4, VL = (T::V_LOADS + 3) / 4;
-    uint32_t koff[KL];
-#pragma unroll
-    for (int x = 0; x < KL; ++x) {
-        const int t = wave + 4 * x;
-        const int P = 64 * t + lane;  // padded chunk slot written by this lane
-        const int r = P / T::KCH, c = P % T::KCH;
-        koff[x] = (t < T::K_LOADS && c < T::CPR) ? (uint32_t)(r * D + c * 8) * 2
-                                                  : kOutOfRange;  // pad: no fetch
-    }
-    // V: lane writes row RPL*t + lane/CPR, physical chunk lane%CPR, which holds
-    // logical chunk (lane%CPR) ^ v_swz(row); v_swz depends on lane only here.
-    const uint32_t voff = (uint32_t)((lane / T::CPR) * D +
-                                     (((lane % T::CPR) ^ v_swz<D>(lane / T::CPR)) * 8)) * 2;
-    auto load_k = [&](int k0, bf16* dst) {
-#pragma unroll
-        for (int x = 0; x < KL; ++x) {
-            const int t = wave + 4 * x;
-            if (t < T::K_LOADS)
-                load16_lds(kb, koff[x] + (uint32_t)k0 * D * 2, dst + 512 * t);
-        }
+    // ---- the pipeline works on 32-key half tiles: half h holds keys
+    //      32h .. 32h+31 (LDS tile h/2, rows 32*(h%2) ..).  Its scores live in
+    //      one f32x16 (lane: query qi, keys 32h + 8(r/4) + 4hi + r%4) and its
+    //      weights in two bf16x8 B operands (k-steps of 16 keys). -------------
+    //
+    // element mask: only on halves crossing the diagonal or the sequence end;
+    // element r is allowed while its key offset stays below this lane's limit
+    auto needs_mask = [&](int h) {
+        return (CAUSAL && 32 * h + 31 > q0) || 32 * h + 32 > n;
     };
-    auto load_v = [&](int k0, bf16* dst) {
-#pragma unroll
-        for (int x = 0; x < VL; ++x) {
-            const int t = wave + 4 * x;
-            if (t < T::V_LOADS)
-                load16_lds(vb, voff + (uint32_t)(k0 + T::RPL * t) * D * 2, dst + 512 * t);
-        }
-    };
-    auto kbuf = [&](int i) { return lds + (i & 1) * T::K_ELEMS; };
-    auto vbuf = [&](int i) { return lds + 2 * T::K_ELEMS + (i & 1) * T::V_ELEMS; };
-
-    // ---- S^T = K Q^T for one tile: lane holds query qi and keys
-    //      k0 + 32*bb + 8*(r/4) + 4*hi + r%4 ---------------------------------
-    auto scores = [&](const bf16* ks, f32x16* s) {
-        s[0] = f32x16{};
-        s[1] = f32x16{};
-#pragma unroll
-        for (int ss = 0; ss < T::DS; ++ss)
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
-                s[bb] = mfma32(
-                    lds_read16(ks + (32 * bb + l32) * T::KSTR + 16 * ss + 8 * hi),
-                    qreg[ss], s[bb]);
-    };
-
-    // ---- element mask: only on tiles crossing the diagonal or the sequence
-    //      end.  Element (bb, r) is key k0 + 32bb + 8(r/4) + 4hi + r%4; it is
-    //      allowed while that offset stays below this lane's limit. ----------
-    auto needs_mask = [&](int k0) {
-        return (CAUSAL && k0 + T::BC - 1 > qw0) || k0 + T::BC > n;
-    };
-    auto apply_mask = [&](f32x16* s, int k0) {
-        int lim = n - k0;                             // keys before the end
-        if (CAUSAL) lim = min(lim, qi - k0 + 1);      // keys j <= qi
+    auto apply_mask = [&](f32x16& s, int h) {
+        int lim = n - 32 * h;                              // keys before the end
+        if (CAUSAL) lim = min(lim, qi - 32 * h + 1);       // keys j <= qi
         lim -= 4 * hi;
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (32 * bb + 8 * (r / 4) + (r & 3) >= lim) s[bb][r] = kNegInf;
+        for (int r = 0; r < 16; ++r)
+            if (8 * (r / 4) + (r & 3) >= lim) s[r] = kNegInf;
     };
 
-    // ---- online softmax statistics of one score tile: new running maximum
-    //      (lazy), rescale factor, exponentials as bf16 B operands, row sum --
-    auto softmax = [&](f32x16* s, bf16x8 (&pb)[2][2], float& alpha, bool& upd) {
-        float mx = kNegInf;
+    // online softmax of one half: new running maximum (lazy), rescale factor,
+    // exponentials as bf16 B operands, row sum
+    auto softmax = [&](f32x16& s, bf16x8 (&pb)[2], float& alpha, bool& upd) {
+        float t4[4];
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bb][r]);
-        mx = fmaxf(mx, xor32(mx)) * p.c;  // tile row maximum, base-2 units
-        upd = mx > m_run + kLazyRescale;  // the first live tile always moves it
+        for (int i = 0; i < 4; ++i)
+            t4[i] = fmaxf(fmaxf(s[4 * i], s[4 * i + 1]), fmaxf(s[4 * i + 2], s[4 * i + 3]));
+        float mx = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
+        mx = pair_max(mx) * p.c;  // row maximum of the half, base-2 units
+        upd = mx > m_run + kLazyRescale;  // the first live half always moves it
         const float m_new = upd ? mx : m_run;
         const float m_use = (m_new == kNegInf) ? 0.f : m_new;  // no key yet: no NaN
         alpha = upd ? exp2_fast(m_run - m_use) : 1.f;
         m_run = m_new;
-        float rs = 0.f;
+        // exponentials in place, summed in fp32 in four independent chains
+        // (summing the bf16-rounded weights instead would put up to 2^-9
+        // relative error into l when one weight dominates and the reference
+        // maximum is stale), then packed to bf16
+        float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
+        for (int r = 0; r < 16; ++r) {
+            s[r] = exp2_fast(__builtin_fmaf(s[r], p.c, -m_use));
+            rs[r & 3] += s[r];
+        }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = exp2_fast(__builtin_fmaf(s[bb][r], p.c, -m_use));
-                rs += e;
-                pb[bb][r >> 3][r & 7] = to_bf16(e);
-            }
-        l_run = __builtin_fmaf(l_run, alpha, rs);
-    };
-
-    // ---- O^T += V^T P^T; V^T delivered by transpose reads of row-major V.
-    //      Rows kr, kr+8 (kr = 32bb + 16t + 4hi + i16/4) share v_swz(kr), so
-    //      the swizzled column depends on the lane and e only. ---------------
-    auto pv = [&](const bf16x8 (&pb)[2][2], const bf16* vs) {
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int kr = 32 * bb + 16 * t + 4 * hi + (i16 >> 2);
-#pragma unroll
-                for (int e = 0; e < T::DB; ++e) {
-                    const int dcol = 32 * e + 16 * (g & 1) + 4 * (i16 & 3);
-                    const int col = (((dcol >> 3) ^ v_swz<D>(kr)) << 3) + (dcol & 7);
-                    const bf16x4 va = lds_read_tr(vs + kr * D + col);
-                    const bf16x4 vc = lds_read_tr(vs + (kr + 8) * D + col);
-                    acc[e] = mfma32(cat(va, vc), pb[bb][t], acc[e]);
-                }
-            }
+        for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = to_bf16(s[r]);
+        l_run = __builtin_fmaf(l_run, alpha, (rs[0] + rs[1]) + (rs[2] + rs[3]));
     };
     auto rescale = [&](float alpha, bool upd) {
         if (__any(upd)) {
@@ -272,54 +267,112 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         }
     };
 
-    // ---- software pipeline: during tile j, K_{j+1} is already in LDS, so
-    //      S_{j+1} = K_{j+1} Q^T (MFMA) and the softmax of S_j (VALU) form one
-    //      branch-free block the scheduler can interleave.  K_{j+2} and V_{j+1}
-    //      load into the buffers no wave reads this iteration, so one barrier
-    //      per tile suffices.  The last tile is peeled off the loop. ---------
+    // MFMA operands.  S: A = K rows (ds_read_b128), B = Q registers.  P.V:
+    // A = V^T by transpose reads, B = P^T; rows kr, kr+8 (kr = 16bt + 4hi +
+    // i16/4) share v_swz(kr), so the swizzled column depends on lane and e.
+    auto k_op = [&](const bf16* ks, int half, int ss) {
+        return lds_read16(ks + (32 * half + l32) * T::KSTR + 16 * ss + 8 * hi);
+    };
+    auto v_op = [&](const bf16* vs, int bt, int e) {
+        const int kr = 16 * bt + 4 * hi + (i16 >> 2);
+        const int dcol = 32 * e + 16 * (g & 1) + 4 * (i16 & 3);
+        const int col = (((dcol >> 3) ^ v_swz<D>(kr)) << 3) + (dcol & 7);
+        return cat(lds_read_tr(vs + kr * D + col), lds_read_tr(vs + (kr + 8) * D + col));
+    };
+
+    // ---- one half-step: S of the next half (DS MFMAs, rows 32*kh of ks) if
+    //      DO_S, P.V of the previous half (2*DB MFMAs, rows 32*vh of vs, with
+    //      pb_prev) if DO_PV, and the softmax of s_cur into pb_new if DO_SM.
+    //      MFMAs alternate S / P.V (independent neighbours) and every operand
+    //      is requested from LDS four MFMAs ahead; the compiler interleaves
+    //      the softmax VALU work (pinning a fixed pattern measured slower). --
+    auto half_step = [&](auto do_s, auto do_pv, auto do_sm, const bf16* ks, int kh,
+                         const bf16* vs, int vh, f32x16& s_cur, f32x16& s_nxt,
+                         const bf16x8 (&pb_prev)[2], bf16x8 (&pb_new)[2], float& alpha,
+                         bool& upd) {
+        constexpr bool DO_S = decltype(do_s)::value, DO_PV = decltype(do_pv)::value;
+        constexpr bool DO_SM = decltype(do_sm)::value;
+        constexpr int NS = DO_S ? T::DS : 0, NP = DO_PV ? 2 * T::DB : 0;
+        constexpr int NM = NS + NP;
+        constexpr bool MIX = DO_S && DO_PV;  // NS == NP: alternate
+        auto kind_s = [](int i) { return MIX ? (i & 1) == 0 : DO_S; };
+        auto fetch = [&](int i) -> bf16x8 {
+            if (kind_s(i)) return k_op(ks, kh, MIX ? i >> 1 : i);
+            const int k = MIX ? i >> 1 : i;  // P.V k-step t = k / DB, block e = k % DB
+            return v_op(vs, 2 * vh + k / T::DB, k % T::DB);
+        };
+        auto apply = [&](int i, bf16x8 a) {
+            if (kind_s(i)) {
+                s_nxt = mfma32(a, qreg[MIX ? i >> 1 : i], s_nxt);
+            } else {
+                const int k = MIX ? i >> 1 : i;
+                acc[k % T::DB] = mfma32(a, pb_prev[k / T::DB], acc[k % T::DB]);
+            }
+        };
+        if constexpr (DO_S) s_nxt = f32x16{};
+        constexpr int PF = 4;  // operand read distance, in MFMAs
+        bf16x8 op[NM > 0 ? NM : 1];
+#pragma unroll
+        for (int i = 0; i < PF && i < NM; ++i) op[i] = fetch(i);
+        if constexpr (DO_SM) softmax(s_cur, pb_new, alpha, upd);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            if (i + PF < NM) op[i + PF] = fetch(i + PF);
+            apply(i, op[i]);
+        }
+    };
+
+    // ---- prologue: K_0, K_1, V_0 -> LDS; S of half 0; half-step 0 (S of
+    //      half 1 with the softmax of half 0) -------------------------------
     load_k(0, kbuf(0));
-    load_v(0, vbuf(0));
     if (nkt > 1) load_k(T::BC, kbuf(1));
+    load_v(0, vbuf(0));
     __builtin_amdgcn_s_waitcnt(0);  // Q registers and the first tiles landed
     __syncthreads();
+    f32x16 sA, sB;  // scores of even / odd halves
+    bf16x8 pA[2], pB[2];  // weights of even / odd halves
+    float alpha;
+    bool upd;
+    sA = f32x16{};
+#pragma unroll
+    for (int ss = 0; ss < T::DS; ++ss) sA = mfma32(k_op(kbuf(0), 0, ss), qreg[ss], sA);
+    if (needs_mask(0)) apply_mask(sA, 0);
+    half_step(True{}, False{}, True{}, kbuf(0), 1, nullptr, 0, sA, sB, pB, pA, alpha, upd);
+    __syncthreads();  // K_0 is consumed before tile-step 0 reloads its buffer
 
-    f32x16 s_cur[2], s_nxt[2];
-    scores(kbuf(0), s_cur);  // tile 0 is never in any wave's future
+    // ---- tile-steps.  Tile-step j runs half-steps 2j+1 (odd: softmax sB ->
+    //      pB, S of half 2j+2 -> sA, P.V of half 2j with pA) and 2j+2 (even:
+    //      softmax sA -> pA, S of half 2j+3 -> sB, P.V of half 2j+1 with pB).
+    //      It reads only K tile j+1 and V tile j, so K_{j+2} and V_{j+1} load
+    //      into the other buffers during it; one barrier ends it. ----------
     for (int j = 0; j + 1 < nkt; ++j) {
-        const int k0 = j * T::BC;
-        if (j + 2 < nkt) load_k(k0 + 2 * T::BC, kbuf(j));  // K_j consumed last iteration
-        load_v(k0 + T::BC, vbuf(j + 1));                    // V_{j-1} likewise
-        // a wave whose rows all precede tile j is done (its later tiles too)
-        if (!(CAUSAL && k0 > qw0 + 31)) {
-            if (needs_mask(k0)) apply_mask(s_cur, k0);
-            bf16x8 pb[2][2];
-            float alpha;
-            bool upd;
-            scores(kbuf(j + 1), s_nxt);
-            softmax(s_cur, pb, alpha, upd);
-            rescale(alpha, upd);
-            pv(pb, vbuf(j));
-            s_cur[0] = s_nxt[0];
-            s_cur[1] = s_nxt[1];
-        }
-        wait_vmem();  // this iteration's tile loads have landed in LDS
+        if (j + 2 < nkt) load_k((j + 2) * T::BC, kbuf(j));
+        load_v((j + 1) * T::BC, vbuf(j + 1));
+        const bf16* ks = kbuf(j + 1);
+        const bf16* vs = vbuf(j);
+        if (needs_mask(2 * j + 1)) apply_mask(sB, 2 * j + 1);
+        half_step(True{}, True{}, True{}, ks, 0, vs, 0, sB, sA, pA, pB, alpha, upd);
+        rescale(alpha, upd);
+        if (needs_mask(2 * j + 2)) apply_mask(sA, 2 * j + 2);
+        half_step(True{}, True{}, True{}, ks, 1, vs, 1, sA, sB, pB, pA, alpha, upd);
+        rescale(alpha, upd);
+        wait_vmem();  // K_{j+2} and V_{j+1} landed
         __syncthreads();
     }
+    // last tile-step j = nkt - 1: softmax of half 2nkt-1 with P.V of half
+    // 2nkt-2, then P.V of half 2nkt-1
     {
-        const int j = nkt - 1, k0 = j * T::BC;
-        if (!(CAUSAL && k0 > qw0 + 31)) {
-            if (needs_mask(k0)) apply_mask(s_cur, k0);
-            bf16x8 pb[2][2];
-            float alpha;
-            bool upd;
-            softmax(s_cur, pb, alpha, upd);
-            rescale(alpha, upd);
-            pv(pb, vbuf(j));
-        }
+        const int j = nkt - 1;
+        const bf16* vs = vbuf(j);
+        if (needs_mask(2 * j + 1)) apply_mask(sB, 2 * j + 1);
+        half_step(False{}, True{}, True{}, nullptr, 0, vs, 0, sB, sA, pA, pB, alpha, upd);
+        rescale(alpha, upd);
+        half_step(False{}, True{}, False{}, nullptr, 0, vs, 1, sA, sB, pB, pA, alpha, upd);
     }
+    __syncthreads();  // LDS reads done before the next tile of the unit reloads
 
     // epilogue: O = u / l (bf16), L = m + ln l (natural log, scaled units)
-    const float l_tot = l_run + xor32(l_run);
+    const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
     for (int e = 0; e < T::DB; ++e)
@@ -334,6 +387,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         const float L = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : kNegInf;
         store4(lb, (uint32_t)qi * 4, __builtin_bit_cast(uint32_t, L));
     }
+    }  // query tiles of the unit
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
@@ -348,9 +402,10 @@ hipError_t run_fwd(const FwdArgs& a, hipStream_t stream) {
     p.cu = a.cu;
     p.H = a.H;
     p.N = a.N;
-    p.n_qt = (a.max_seqlen + T::BR - 1) / T::BR;
+    const int n_qt = (a.max_seqlen + T::BR - 1) / T::BR;
+    p.per_head = CAUSAL ? (n_qt + 1) / 2 : n_qt;
     p.c = (float)((double)a.scale * 1.4426950408889634);
-    const int64_t units = (int64_t)p.n_qt * a.H * a.B;
+    const int64_t units = (int64_t)p.per_head * a.H * a.B;
     hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)units),
                        dim3(T::THREADS), 0, stream, p);
     return hipGetLastError();
