@@ -79,6 +79,13 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 // s_waitcnt vmcnt(0) only (gfx9 encoding: expcnt and lgkmcnt left at max).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Workgroup barrier without the release/acquire fences of __syncthreads: the
+// caller has already waited (s_waitcnt) for whatever other waves must see,
+// e.g. tiles DMA-loaded into LDS.  The memory clobber keeps the compiler from
+// moving memory accesses across it.  (The fences would force vmcnt(0), also
+// for loads deliberately left in flight across the barrier.)
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
 __device__ __forceinline__ float loadf(Buf b, uint32_t off) {
     return __builtin_bit_cast(float,
                               __builtin_amdgcn_raw_buffer_load_b32(b.r, off, 0, 0));

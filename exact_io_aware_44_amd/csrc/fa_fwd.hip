@@ -70,7 +70,6 @@ struct FwdTile {
     static constexpr int V_LOADS = BC * CPR / 64;
     static constexpr int K_ELEMS = K_LOADS * 512;  // >= BC * KSTR
     static constexpr int V_ELEMS = BC * D;
-    static constexpr int LDS_ELEMS = 2 * K_ELEMS + 2 * V_ELEMS;  // K x2, V x2
     static constexpr int DS = D / 16;      // MFMA k-steps across the head width
     static constexpr int DB = D / 32;      // 32-wide blocks of the output
     static constexpr int RPL = 64 / CPR;   // V rows per wave-wide load
@@ -118,7 +117,13 @@ using False = std::false_type;
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     using T = FwdTile<D>;
-    __shared__ __attribute__((aligned(16))) bf16 lds[T::LDS_ELEMS];
+    // Separate LDS objects per buffer, always selected statically, so the
+    // compiler can tell a tile being read from the tile a DMA is filling and
+    // does not hold the reads back until every load has landed.
+    __shared__ __attribute__((aligned(16))) bf16 k_lds0[T::K_ELEMS];
+    __shared__ __attribute__((aligned(16))) bf16 k_lds1[T::K_ELEMS];
+    __shared__ __attribute__((aligned(16))) bf16 v_lds0[T::V_ELEMS];
+    __shared__ __attribute__((aligned(16))) bf16 v_lds1[T::V_ELEMS];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -191,8 +196,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
             load16_lds(vb, voff + (uint32_t)(k0 + T::RPL * t) * D * 2, dst + 512 * t);
         }
     };
-    auto kbuf = [&](int i) { return lds + (i & 1) * T::K_ELEMS; };
-    auto vbuf = [&](int i) { return lds + 2 * T::K_ELEMS + (i & 1) * T::V_ELEMS; };
 
     for (int rep = 0; rep < ntiles; ++rep) {
     const int q0 = (rep == 0 ? tile0 : tile1) * T::BR;
@@ -324,50 +327,58 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 
     // ---- prologue: K_0, K_1, V_0 -> LDS; S of half 0; half-step 0 (S of
     //      half 1 with the softmax of half 0) -------------------------------
-    load_k(0, kbuf(0));
-    if (nkt > 1) load_k(T::BC, kbuf(1));
-    load_v(0, vbuf(0));
-    __builtin_amdgcn_s_waitcnt(0);  // Q registers and the first tiles landed
-    __syncthreads();
+    load_k(0, k_lds0);
+    if (nkt > 1) load_k(T::BC, k_lds1);
+    load_v(0, v_lds0);
+    wait_vmem();  // Q registers and the first tiles landed
+    barrier_only();
     f32x16 sA, sB;  // scores of even / odd halves
     bf16x8 pA[2], pB[2];  // weights of even / odd halves
     float alpha;
     bool upd;
     sA = f32x16{};
 #pragma unroll
-    for (int ss = 0; ss < T::DS; ++ss) sA = mfma32(k_op(kbuf(0), 0, ss), qreg[ss], sA);
+    for (int ss = 0; ss < T::DS; ++ss) sA = mfma32(k_op(k_lds0, 0, ss), qreg[ss], sA);
     if (needs_mask(0)) apply_mask(sA, 0);
-    half_step(True{}, False{}, True{}, kbuf(0), 1, nullptr, 0, sA, sB, pB, pA, alpha, upd);
+    half_step(True{}, False{}, True{}, k_lds0, 1, nullptr, 0, sA, sB, pB, pA, alpha, upd);
     __syncthreads();  // K_0 is consumed before tile-step 0 reloads its buffer
 
     // ---- tile-steps.  Tile-step j runs half-steps 2j+1 (odd: softmax sB ->
     //      pB, S of half 2j+2 -> sA, P.V of half 2j with pA) and 2j+2 (even:
     //      softmax sA -> pA, S of half 2j+3 -> sB, P.V of half 2j+1 with pB).
-    //      It reads only K tile j+1 and V tile j, so K_{j+2} and V_{j+1} load
-    //      into the other buffers during it; one barrier ends it. ----------
-    for (int j = 0; j + 1 < nkt; ++j) {
-        if (j + 2 < nkt) load_k((j + 2) * T::BC, kbuf(j));
-        load_v((j + 1) * T::BC, vbuf(j + 1));
-        const bf16* ks = kbuf(j + 1);
-        const bf16* vs = vbuf(j);
+    //      It reads only K tile j+1 (buffer (j+1)%2) and V tile j (buffer
+    //      j%2), so K_{j+2} and V_{j+1} load into the other buffers during
+    //      it; one barrier ends it. ---------------------------------------
+    // The buffer pointers are __restrict__: the tile a DMA is filling never
+    // overlaps a tile being read, which lets the compiler leave the loads in
+    // flight while the reads proceed.
+    auto tile_step = [&](int j, const bf16* __restrict__ k_rd, const bf16* __restrict__ v_rd,
+                         bf16* __restrict__ k_wr, bf16* __restrict__ v_wr) {
+        if (j + 2 < nkt) load_k((j + 2) * T::BC, k_wr);
+        load_v((j + 1) * T::BC, v_wr);
         if (needs_mask(2 * j + 1)) apply_mask(sB, 2 * j + 1);
-        half_step(True{}, True{}, True{}, ks, 0, vs, 0, sB, sA, pA, pB, alpha, upd);
+        half_step(True{}, True{}, True{}, k_rd, 0, v_rd, 0, sB, sA, pA, pB, alpha, upd);
         rescale(alpha, upd);
         if (needs_mask(2 * j + 2)) apply_mask(sA, 2 * j + 2);
-        half_step(True{}, True{}, True{}, ks, 1, vs, 1, sA, sB, pB, pA, alpha, upd);
+        half_step(True{}, True{}, True{}, k_rd, 1, v_rd, 1, sA, sB, pB, pA, alpha, upd);
         rescale(alpha, upd);
         wait_vmem();  // K_{j+2} and V_{j+1} landed
-        __syncthreads();
+        barrier_only();
+    };
+    for (int j = 0; j + 1 < nkt; ++j) {
+        const bool odd = j & 1;
+        tile_step(j, odd ? k_lds0 : k_lds1, odd ? v_lds1 : v_lds0, odd ? k_lds1 : k_lds0,
+                  odd ? v_lds0 : v_lds1);
     }
     // last tile-step j = nkt - 1: softmax of half 2nkt-1 with P.V of half
     // 2nkt-2, then P.V of half 2nkt-1
     {
         const int j = nkt - 1;
-        const bf16* vs = vbuf(j);
+        const bf16* v_rd = (j & 1) ? v_lds1 : v_lds0;
         if (needs_mask(2 * j + 1)) apply_mask(sB, 2 * j + 1);
-        half_step(False{}, True{}, True{}, nullptr, 0, vs, 0, sB, sA, pA, pB, alpha, upd);
+        half_step(False{}, True{}, True{}, nullptr, 0, v_rd, 0, sB, sA, pA, pB, alpha, upd);
         rescale(alpha, upd);
-        half_step(False{}, True{}, False{}, nullptr, 0, vs, 1, sA, sB, pB, pA, alpha, upd);
+        half_step(False{}, True{}, False{}, nullptr, 0, v_rd, 1, sA, sB, pB, pA, alpha, upd);
     }
     __syncthreads();  // LDS reads done before the next tile of the unit reloads
 
