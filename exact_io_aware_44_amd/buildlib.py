@@ -24,7 +24,11 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE,
 
 # Per-file extras.  The forward kernel's inputs are finite by contract (the
 # mask uses -inf, never NaN), so fmaxf needs no NaN canonicalisation there.
-EXTRA = {"fa_fwd.hip": ["-fno-honor-nans"]}
+# The backward kernels fit in 256 VGPRs; MFMAs that write VGPRs keep the
+# compiler from parking their results in AGPRs and copying them back and
+# forth around every VALU use.
+EXTRA = {"fa_fwd.hip": ["-fno-honor-nans"],
+         "fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str, obj_dir: str) -> str:

@@ -42,9 +42,11 @@ int validate_fwd(const void* q, const void* k, const void* v, const void* o,
     return check_slice(N, D);
 }
 
+// Two fp32 values per query row (D_i = dO_i . O_i and -L_i log2 e), stored
+// as two [B, H, N] regions, each padded to 256 bytes.
 size_t workspace_bytes(int B, int H, int N) {
     const size_t rows = (size_t)B * H * N;
-    return (rows * sizeof(float) + 255) & ~(size_t)255;
+    return 2 * ((rows * sizeof(float) + 255) & ~(size_t)255);
 }
 
 }  // namespace

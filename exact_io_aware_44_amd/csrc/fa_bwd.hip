@@ -47,18 +47,39 @@ struct BwdParams {
     bf16* dq;
     bf16* dk;
     bf16* dv;
-    float* dsum;
+    float* dd;     // [B, H, N]  D_i = dO_i . O_i
+    float* nl2;    // [B, H, N]  -L_i * log2(e)
     int H, N;
-    float c;      // scale * log2(e)
+    int per_head;  // dK/dV units per (batch, head): key tiles, or pairs if causal
+    float c;       // scale * log2(e)
     float scale;
 };
 
+// Direct global -> LDS load of one dword per lane (lane i writes M0 + 4*i).
+__device__ __forceinline__ void load4_lds(Buf b, uint32_t off, void* lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (FA_LDS void*)lds_wave_base, 4, off, 0,
+                                             0, 0);
+}
+// s_waitcnt vmcnt(0) lgkmcnt(0): this wave's loads (global and LDS) are done.
+__device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0070); }
+
+// Workgroup i of a 1-D grid runs on XCD i % 8; this remap gives each XCD a
+// contiguous, head-major range of units so one head's tiles stay in one L2.
+__device__ __forceinline__ void unit_of(int i, int total, int per_head, int& head,
+                                        int& idx) {
+    const int L = (total & 7) == 0 ? (i & 7) * (total >> 3) + (i >> 3) : i;
+    head = L / per_head;
+    idx = L - head * per_head;
+}
+
 // ---------------------------------------------------------------------------
-// 1. D_i = dO_i . O_i  (fp32 sum of exact bf16 products)
+// 1. Per-row constants: D_i = dO_i . O_i (fp32 sum of exact bf16 products)
+//    and -L_i log2(e), the exponent offset that turns a score into its weight.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void dsum_kernel(const bf16* o, const bf16* dout,
-                                                   float* dsum, int64_t rows) {
+                                                   const float* lse, float* dd, float* nl2,
+                                                   int64_t rows) {
     constexpr int LPR = D / 8;  // lanes per row, 16 bytes each
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t row = gid / LPR;
@@ -72,189 +93,231 @@ __global__ __launch_bounds__(256) void dsum_kernel(const bf16* o, const bf16* do
     }
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (row < rows && part == 0) dsum[row] = acc;
+    if (row < rows && part == 0) {
+        dd[row] = acc;
+        nl2[row] = -lse[row] * kLog2e;
+    }
 }
 
 // ---------------------------------------------------------------------------
-// 2. dK, dV: unit = (batch, head, 128-key tile); 4 waves x 32 keys.
+// 2. dK, dV: unit = (batch, head, 128-key tile); wave w owns keys 32w..32w+31
+//    of the tile and keeps their dK^T, dV^T accumulators in registers; K and V
+//    sit in LDS for the whole unit while 64-query stages of Q, dO,
+//    -L log2 e and D stream through double-buffered LDS.
 // ---------------------------------------------------------------------------
 template <int D>
 struct KvTile {
-    static constexpr int BK = 128;       // keys per unit
-    static constexpr int BQ = 64;        // queries per streamed tile
+    static constexpr int BK = 128;                 // keys per unit
+    static constexpr int BQ = 64;                  // queries per streamed stage
     static constexpr int THREADS = 256;
-    static constexpr int QSTR = D + 8;   // Q / dO row pitch in LDS (elements)
-    static constexpr int T_ELEMS = BQ * QSTR;
-    // stage layout: Q tile, dO tile (bf16), then L2 and D (fp32, BQ each)
-    static constexpr int STAGE_BYTES = 2 * T_ELEMS * 2 + 2 * BQ * 4;
-    static constexpr int CPT = BQ * D / 8 / THREADS;
-    static constexpr int DS = D / 16;
-    static constexpr int DB = D / 32;
+    static constexpr int CPR = D / 8;              // 16-byte chunks per row
+    static constexpr int T_ELEMS = BQ * D;         // one Q or dO stage
+    static constexpr int LPW = BQ * CPR / 64 / 4;  // 1 KiB loads per wave per tile
+    static constexpr int RPL = 64 / CPR;           // rows per 1 KiB load
+    static constexpr int DS = D / 16;              // MFMA k-steps across the head width
+    static constexpr int DB = D / 32;              // 32-wide blocks of the head width
+    // K / V of the unit: row pitch padded by one chunk so the 16 rows a
+    // quarter-wave reads with ds_read_b128 land 4 banks apart
+    static constexpr int KSTR = D + 8;
+    static constexpr int KV_ELEMS = BK * KSTR;
+    static constexpr int KV_LOADS = BK * CPR / 64;  // 1 KiB loads per K or V tile
 };
+
+// Q / dO stages are stored with unpadded rows and the 16-byte chunk index of
+// row r XORed with qd_swz(r).  Both read patterns are then free of bank
+// conflicts (64 banks): a quarter-wave ds_read_b128 of one chunk in 16
+// consecutive rows sees 16 distinct XORs, and a half-wave transpose read of 4
+// chunks in 4 consecutive rows sees the 4 rows in 4 distinct chunk groups.
+template <int D>
+__device__ __forceinline__ int qd_swz(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
+                    : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+template <int D>
+__device__ __forceinline__ int qd_off(int r, int chunk) {  // element offset
+    return r * D + ((chunk ^ qd_swz<D>(r)) << 3);
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     using T = KvTile<D>;
-    __shared__ __attribute__((aligned(16))) char lds_raw[2 * T::STAGE_BYTES];
+    // one LDS object per buffer, selected statically, so the compiler can tell
+    // the stage being read from the one a DMA is filling
+    __shared__ __attribute__((aligned(16))) bf16 q_lds0[T::T_ELEMS];
+    __shared__ __attribute__((aligned(16))) bf16 q_lds1[T::T_ELEMS];
+    __shared__ __attribute__((aligned(16))) bf16 do_lds0[T::T_ELEMS];
+    __shared__ __attribute__((aligned(16))) bf16 do_lds1[T::T_ELEMS];
+    __shared__ __attribute__((aligned(16))) float f_lds0[2 * T::BQ];  // -L log2 e, then D
+    __shared__ __attribute__((aligned(16))) float f_lds1[2 * T::BQ];
+    __shared__ __attribute__((aligned(16))) bf16 k_lds[T::KV_ELEMS];
+    __shared__ __attribute__((aligned(16))) bf16 v_lds[T::KV_ELEMS];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5;
     const int g = lane >> 4, i16 = lane & 15;
-    const int kt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    int head, uidx;
+    unit_of(blockIdx.x, gridDim.x, p.per_head, head, uidx);
     const int n = p.N;
-    const int64_t row0 = ((int64_t)b * p.H + h) * n;
+    const int nkt = (n + T::BK - 1) / T::BK;
+    // key tiles of this unit: under causal masking a heavy one (many queries
+    // follow it) and the matching light one, so all units carry equal work
+    int kt0 = uidx, kt1 = -1;
+    if (CAUSAL) {
+        kt1 = nkt - 1 - uidx;
+        if (kt1 < kt0) return;
+        if (kt1 == kt0) kt1 = -1;
+    } else if (kt0 >= nkt) {
+        return;
+    }
+
+    const int64_t row0 = (int64_t)head * n;
     const uint32_t bytes = (uint32_t)n * D * 2;
     const Buf qb = make_buf(p.q + row0 * D, bytes);
     const Buf kb = make_buf(p.k + row0 * D, bytes);
     const Buf vb = make_buf(p.v + row0 * D, bytes);
     const Buf dob = make_buf(p.dout + row0 * D, bytes);
-    const Buf lb = make_buf(p.lse + row0, (uint32_t)n * 4);
-    const Buf db = make_buf(p.dsum + row0, (uint32_t)n * 4);
+    const Buf nlb = make_buf(p.nl2 + row0, (uint32_t)n * 4);
+    const Buf ddb = make_buf(p.dd + row0, (uint32_t)n * 4);
     const Buf dkb = make_buf(p.dk + row0 * D, bytes);
     const Buf dvb = make_buf(p.dv + row0 * D, bytes);
 
-    const int k0u = kt * T::BK;           // first key of the unit
-    const int kw0 = k0u + 32 * wave;      // first key of this wave
-    const int kj = kw0 + l32;             // key held by this lane
-
-    // K and V as B operands (lane: row kj, columns 16s + 8hi + 0..7)
-    bf16x8 kreg[T::DS], vreg[T::DS];
+    // ---- stage movement: wave w issues the 1 KiB loads w*LPW .. w*LPW+LPW-1
+    //      of each tile; lane -> LDS slot is fixed, the global chunk it
+    //      fetches carries the swizzle ----
+    uint32_t qoff[T::LPW];
 #pragma unroll
-    for (int s = 0; s < T::DS; ++s) {
-        const uint32_t off = ((uint32_t)kj * D + 16 * s + 8 * hi) * 2;
-        kreg[s] = __builtin_bit_cast(bf16x8, load16(kb, off));
-        vreg[s] = __builtin_bit_cast(bf16x8, load16(vb, off));
+    for (int x = 0; x < T::LPW; ++x) {
+        const int L = wave * T::LPW + x;
+        const int r = L * T::RPL + lane / T::CPR;
+        const int pc = lane % T::CPR;
+        qoff[x] = (uint32_t)(r * D + ((pc ^ qd_swz<D>(r)) << 3)) * 2;
     }
-
-    f32x16 dv[T::DB], dk[T::DB];
+    auto load_stage = [&](int q0, bf16* __restrict__ qd, bf16* __restrict__ dod,
+                          float* __restrict__ fd) __attribute__((always_inline)) {
 #pragma unroll
-    for (int e = 0; e < T::DB; ++e) {
-        dv[e] = f32x16{};
-        dk[e] = f32x16{};
-    }
-
-    const int qt0 = CAUSAL ? k0u / T::BQ : 0;  // earlier queries see none of these keys
-    const int nqt = (n + T::BQ - 1) / T::BQ;
-
-    u32x4 qreg_g[T::CPT], doreg_g[T::CPT];
-    float lval = 0.f;
-    auto gload = [&](int q0) {
-#pragma unroll
-        for (int i = 0; i < T::CPT; ++i) {
-            const int c = tid + T::THREADS * i;
-            const int r = c / (D / 8), cc = c % (D / 8);
-            const uint32_t off = ((uint32_t)(q0 + r) * D + cc * 8) * 2;
-            qreg_g[i] = load16(qb, off);
-            doreg_g[i] = load16(dob, off);
+        for (int x = 0; x < T::LPW; ++x) {
+            const int L = wave * T::LPW + x;
+            load16_lds(qb, qoff[x] + (uint32_t)q0 * D * 2, qd + 512 * L);
+            load16_lds(dob, qoff[x] + (uint32_t)q0 * D * 2, dod + 512 * L);
         }
-        if (tid < T::BQ) lval = loadf(lb, (uint32_t)(q0 + tid) * 4) * kLog2e;
-        else if (tid < 2 * T::BQ) lval = loadf(db, (uint32_t)(q0 + tid - T::BQ) * 4);
-    };
-    auto lstore = [&](int stage) {
-        char* base = lds_raw + stage * T::STAGE_BYTES;
-        bf16* qs = reinterpret_cast<bf16*>(base);
-        bf16* dos = qs + T::T_ELEMS;
-        float* fs = reinterpret_cast<float*>(dos + T::T_ELEMS);
-#pragma unroll
-        for (int i = 0; i < T::CPT; ++i) {
-            const int c = tid + T::THREADS * i;
-            const int r = c / (D / 8), cc = c % (D / 8);
-            lds_write16(qs + r * T::QSTR + cc * 8, qreg_g[i]);
-            lds_write16(dos + r * T::QSTR + cc * 8, doreg_g[i]);
-        }
-        if (tid < 2 * T::BQ) fs[tid] = lval;  // L2 at [0, BQ), D at [BQ, 2BQ)
+        if (wave == 0) load4_lds(nlb, (uint32_t)(q0 + lane) * 4, fd);
+        if (wave == 1) load4_lds(ddb, (uint32_t)(q0 + lane) * 4, fd + T::BQ);
     };
 
-    auto compute = [&](int stage, int q0) {
-        if (CAUSAL && q0 + T::BQ - 1 < kw0) return;  // every query precedes our keys
-        const char* base = lds_raw + stage * T::STAGE_BYTES;
-        const bf16* qs = reinterpret_cast<const bf16*>(base);
-        const bf16* dos = qs + T::T_ELEMS;
-        const float* l2s = reinterpret_cast<const float*>(dos + T::T_ELEMS);
-        const float* dss = l2s + T::BQ;
+    f32x16 dk[T::DB], dv[T::DB];
+    int kw0 = 0, kj = 0;
 
-        // S[query][key] for two 32-query blocks; lane holds key kj and local
-        // queries 32*qb + 8*(r/4) + 4*hi + r%4.
-        f32x16 s[2], dp[2];
+    // One 32-query block of a stage: S = Q K^T and dP = dO V^T (lane: key kj,
+    // local queries 8(r/4) + 4hi + r%4), P = exp2(S c - L log2 e),
+    // dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T
+    // delivered by transpose reads.
+    auto block = [&](const bf16* __restrict__ qs, const bf16* __restrict__ dos,
+                     const float* __restrict__ fs, int q0, int b)
+                     __attribute__((always_inline)) {
+        const int qb0 = q0 + 32 * b;
+        if (CAUSAL && qb0 + 31 < kw0) return;  // every query precedes our keys
+        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int qb2 = 0; qb2 < 2; ++qb2) {
-            s[qb2] = f32x16{};
-            dp[qb2] = f32x16{};
+        for (int ss = 0; ss < T::DS; ++ss) {
+            const int off = qd_off<D>(32 * b + l32, 2 * ss + hi);
+            const int koff = (32 * wave + l32) * T::KSTR + 16 * ss + 8 * hi;
+            s = mfma32(lds_read16(qs + off), lds_read16(k_lds + koff), s);
+            dp = mfma32(lds_read16(dos + off), lds_read16(v_lds + koff), dp);
+        }
+        const bool need_mask = CAUSAL && qb0 < kw0 + 31;
+        const int tm = kj - qb0 - 4 * hi;  // masked where tm > local query offset
+        bf16x8 pb[2], sb[2];
 #pragma unroll
-            for (int ss = 0; ss < T::DS; ++ss) {
-                const int off = (32 * qb2 + l32) * T::QSTR + 16 * ss + 8 * hi;
-                s[qb2] = mfma32(lds_read16(qs + off), kreg[ss], s[qb2]);
-                dp[qb2] = mfma32(lds_read16(dos + off), vreg[ss], dp[qb2]);
+        for (int a = 0; a < 4; ++a) {
+            const f32x4 nl = *reinterpret_cast<const f32x4*>(fs + 32 * b + 8 * a + 4 * hi);
+            const f32x4 dd = *reinterpret_cast<const f32x4*>(fs + T::BQ + 32 * b + 8 * a + 4 * hi);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 4 * a + x;
+                float pv = exp2_fast(__builtin_fmaf(s[r], p.c, nl[x]));
+                if (need_mask) pv = tm > 8 * a + x ? 0.f : pv;
+                const float dsv = pv * (dp[r] - dd[x]);
+                pb[r / 8][r % 8] = to_bf16(pv);
+                sb[r / 8][r % 8] = to_bf16(dsv);
             }
         }
-        const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (q0 + T::BQ > n);
-        // P = exp2(S c - L2), dS = P (dP - D)
-        bf16x8 pb[2][2], sb[2][2];
 #pragma unroll
-        for (int qb2 = 0; qb2 < 2; ++qb2)
+        for (int e = 0; e < T::DB; ++e)
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int lq = 32 * qb2 + 8 * r4 + 4 * hi;  // first of 4 local queries
-                const f32x4 l2 = *reinterpret_cast<const f32x4*>(l2s + lq);
-                const f32x4 dd = *reinterpret_cast<const f32x4*>(dss + lq);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int r = 4 * r4 + x;
-                    float pv = exp2_fast(__builtin_fmaf(s[qb2][r], p.c, -l2[x]));
-                    if (need_mask) {
-                        const int qi = q0 + lq + x;
-                        if ((CAUSAL && kj > qi) || qi >= n) pv = 0.f;
-                    }
-                    const float dsv = pv * (dp[qb2][r] - dd[x]);
-                    pb[qb2][r / 8][r % 8] = to_bf16(pv);
-                    sb[qb2][r / 8][r % 8] = to_bf16(dsv);
-                }
+            for (int t = 0; t < 2; ++t) {
+                const int rr = 32 * b + 16 * t + 4 * hi + (i16 >> 2);
+                const int cc = 4 * e + 2 * (g & 1) + ((i16 & 3) >> 1);
+                const int o0 = qd_off<D>(rr, cc) + 4 * (i16 & 1);
+                const int o1 = qd_off<D>(rr + 8, cc) + 4 * (i16 & 1);
+                const bf16x8 doT = cat(lds_read_tr(dos + o0), lds_read_tr(dos + o1));
+                dv[e] = mfma32(doT, pb[t], dv[e]);
+                const bf16x8 qT = cat(lds_read_tr(qs + o0), lds_read_tr(qs + o1));
+                dk[e] = mfma32(qT, sb[t], dk[e]);
             }
-        // dV^T += dO^T P and dK^T += Q^T dS (A operands by transpose reads)
+    };
+    auto step = [&](int qt, bool more, const bf16* __restrict__ qs,
+                    const bf16* __restrict__ dos, const float* __restrict__ fs,
+                    bf16* __restrict__ qn, bf16* __restrict__ don, float* __restrict__ fn)
+                    __attribute__((always_inline)) {
+        if (more) load_stage((qt + 1) * T::BQ, qn, don, fn);
+        block(qs, dos, fs, qt * T::BQ, 0);
+        // keep the two blocks apart: interleaving them would need more
+        // registers than a wave has
+        __builtin_amdgcn_sched_barrier(0);
+        block(qs, dos, fs, qt * T::BQ, 1);
+        wait_vmem_lds();  // next stage landed; this stage's reads are done
+        barrier_only();
+    };
+
+    for (int rep = 0; rep < 2; ++rep) {
+        const int kt = rep == 0 ? kt0 : kt1;
+        if (kt < 0) break;
+        const int k0u = kt * T::BK;
+        kw0 = k0u + 32 * wave;
+        kj = kw0 + l32;
+        // K and V of the tile into LDS (rows padded to KSTR): the padded
+        // layout is not contiguous, so these go through registers
+#pragma unroll
+        for (int x = 0; x < T::KV_LOADS / 4; ++x) {
+            const int c = 64 * (wave + 4 * x) + lane;  // chunk index in the tile
+            const int r = c / T::CPR, cc = c % T::CPR;
+            const uint32_t off = ((uint32_t)(k0u + r) * D + cc * 8) * 2;
+            lds_write16(k_lds + r * T::KSTR + cc * 8, load16(kb, off));
+            lds_write16(v_lds + r * T::KSTR + cc * 8, load16(vb, off));
+        }
 #pragma unroll
         for (int e = 0; e < T::DB; ++e) {
-            const int dcol = 32 * e + 16 * (g & 1) + 4 * (i16 & 3);
-#pragma unroll
-            for (int qb2 = 0; qb2 < 2; ++qb2)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int qr = 32 * qb2 + 16 * t + 4 * hi + (i16 >> 2);
-                    const bf16x8 doT = cat(lds_read_tr(dos + qr * T::QSTR + dcol),
-                                           lds_read_tr(dos + (qr + 8) * T::QSTR + dcol));
-                    dv[e] = mfma32(doT, pb[qb2][t], dv[e]);
-                    const bf16x8 qT = cat(lds_read_tr(qs + qr * T::QSTR + dcol),
-                                          lds_read_tr(qs + (qr + 8) * T::QSTR + dcol));
-                    dk[e] = mfma32(qT, sb[qb2][t], dk[e]);
-                }
+            dv[e] = f32x16{};
+            dk[e] = f32x16{};
         }
-    };
-
-    if (qt0 < nqt) {
-        gload(qt0 * T::BQ);
-        lstore(0);
-        __syncthreads();
-        for (int it = 0, qt = qt0; qt < nqt; ++qt, ++it) {
+        // under causal masking queries before the key tile see none of it
+        const int qt_begin = CAUSAL ? k0u / T::BQ : 0;
+        const int nqt = (n + T::BQ - 1) / T::BQ;
+        load_stage(qt_begin * T::BQ, q_lds0, do_lds0, f_lds0);
+        wait_vmem_lds();
+        barrier_only();
+        for (int qt = qt_begin; qt < nqt; ++qt) {
             const bool more = qt + 1 < nqt;
-            if (more) gload((qt + 1) * T::BQ);
-            compute(it & 1, qt * T::BQ);
-            if (more) lstore((it + 1) & 1);
-            __syncthreads();
+            const bool odd = (qt - qt_begin) & 1;
+            step(qt, more, odd ? q_lds1 : q_lds0, odd ? do_lds1 : do_lds0,
+                 odd ? f_lds1 : f_lds0, odd ? q_lds0 : q_lds1, odd ? do_lds0 : do_lds1,
+                 odd ? f_lds0 : f_lds1);
         }
+        // dV[kj][d], dK[kj][d] = scale * acc (d = 32e + 8(r/4) + 4hi + r%4)
+#pragma unroll
+        for (int e = 0; e < T::DB; ++e)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = 32 * e + 8 * r4 + 4 * hi;
+                const uint32_t off = ((uint32_t)kj * D + d) * 2;
+                store8(dvb, off, pack4(dv[e][4 * r4], dv[e][4 * r4 + 1],
+                                       dv[e][4 * r4 + 2], dv[e][4 * r4 + 3]));
+                store8(dkb, off,
+                       pack4(dk[e][4 * r4] * p.scale, dk[e][4 * r4 + 1] * p.scale,
+                             dk[e][4 * r4 + 2] * p.scale, dk[e][4 * r4 + 3] * p.scale));
+            }
     }
-
-    // dV[kj][d], dK[kj][d] = scale * acc (lane: key kj, d = 32e + 8(r/4) + 4hi + r%4)
-#pragma unroll
-    for (int e = 0; e < T::DB; ++e)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int d = 32 * e + 8 * r4 + 4 * hi;
-            const uint32_t off = ((uint32_t)kj * D + d) * 2;
-            store8(dvb, off, pack4(dv[e][4 * r4], dv[e][4 * r4 + 1],
-                                   dv[e][4 * r4 + 2], dv[e][4 * r4 + 3]));
-            store8(dkb, off,
-                   pack4(dk[e][4 * r4] * p.scale, dk[e][4 * r4 + 1] * p.scale,
-                         dk[e][4 * r4 + 2] * p.scale, dk[e][4 * r4 + 3] * p.scale));
-        }
 }
 
 // ---------------------------------------------------------------------------
@@ -291,8 +354,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p, int n_qt) {
     const Buf kb = make_buf(p.k + row0 * D, bytes);
     const Buf vb = make_buf(p.v + row0 * D, bytes);
     const Buf dob = make_buf(p.dout + row0 * D, bytes);
-    const Buf lb = make_buf(p.lse + row0, (uint32_t)n * 4);
-    const Buf db = make_buf(p.dsum + row0, (uint32_t)n * 4);
+    const Buf nlb = make_buf(p.nl2 + row0, (uint32_t)n * 4);
+    const Buf ddb = make_buf(p.dd + row0, (uint32_t)n * 4);
     const Buf dqb = make_buf(p.dq + row0 * D, bytes);
 
     const int qw0 = q0 + 32 * wave;
@@ -305,8 +368,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p, int n_qt) {
         qreg[s] = __builtin_bit_cast(bf16x8, load16(qb, off));
         doreg[s] = __builtin_bit_cast(bf16x8, load16(dob, off));
     }
-    const float l2 = loadf(lb, (uint32_t)qi * 4) * kLog2e;
-    const float dd = loadf(db, (uint32_t)qi * 4);
+    const float nl2 = loadf(nlb, (uint32_t)qi * 4);
+    const float dd = loadf(ddb, (uint32_t)qi * 4);
 
     const int kend = CAUSAL ? min(n, q0 + T::BR) : n;
     const int nkt = (kend + T::BC - 1) / T::BC;
@@ -360,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p, int n_qt) {
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float pv = exp2_fast(__builtin_fmaf(s[bb][r], p.c, -l2));
+                float pv = exp2_fast(__builtin_fmaf(s[bb][r], p.c, nl2));
                 if (need_mask) {
                     const int key = k0 + 32 * bb + 8 * (r / 4) + 4 * hi + (r & 3);
                     if ((CAUSAL && key > qi) || key >= n) pv = 0.f;
@@ -417,21 +480,24 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream) {
     p.dq = static_cast<bf16*>(a.dq);
     p.dk = static_cast<bf16*>(a.dk);
     p.dv = static_cast<bf16*>(a.dv);
-    p.dsum = a.dsum;
+    const int64_t rows = (int64_t)a.B * a.H * a.N;
+    p.dd = a.ws;
+    p.nl2 = a.ws + ((rows + 63) & ~(int64_t)63);  // second region, 256-byte aligned
     p.H = a.H;
     p.N = a.N;
     p.c = (float)((double)a.scale * 1.4426950408889634);
     p.scale = a.scale;
 
-    const int64_t rows = (int64_t)a.B * a.H * a.N;
     const int64_t threads = rows * (D / 8);
     hipLaunchKernelGGL((dsum_kernel<D>), dim3((unsigned)((threads + 255) / 256)),
-                       dim3(256), 0, stream, p.o, p.dout, p.dsum, rows);
+                       dim3(256), 0, stream, p.o, p.dout, p.lse, p.dd, p.nl2, rows);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
 
     const int nkt = (a.N + KvTile<D>::BK - 1) / KvTile<D>::BK;
-    hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(nkt, a.H, a.B), dim3(256), 0,
+    p.per_head = CAUSAL ? (nkt + 1) / 2 : nkt;
+    const int64_t units = (int64_t)p.per_head * a.H * a.B;
+    hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3((unsigned)units), dim3(256), 0,
                        stream, p);
     err = hipGetLastError();
     if (err != hipSuccess) return err;

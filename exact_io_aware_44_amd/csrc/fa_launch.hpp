@@ -34,7 +34,8 @@ struct BwdArgs {
     void* dq;
     void* dk;
     void* dv;
-    float* dsum;            // workspace: [B, H, N] fp32
+    float* ws;              // workspace: two fp32 [B, H, N] regions, each
+                            // padded to 256 bytes (D_i, then -L_i log2 e)
     int B, H, N, D;
     float scale;
     bool causal;

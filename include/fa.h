@@ -116,8 +116,9 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes (0 if the sizes
- * are invalid).  The workspace holds one float32 per query row
- * (D_i = <dO_i, O_i>), padded to 256 bytes.
+ * are invalid).  The workspace holds two float32 values per query row,
+ * D_i = <dO_i, O_i> and -L_i * log2(e), as two [B, H, N] regions each
+ * padded to 256 bytes.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int D);
 

@@ -92,8 +92,9 @@ def test_varlen_rejects(lib, kw, code):
 
 
 def test_workspace_size(lib):
-    assert fa.fa_bwd_workspace_size(2, 32, 4096, 128) == 2 * 32 * 4096 * 4
-    assert fa.fa_bwd_workspace_size(1, 1, 3, 64) == 256  # padded to 256 bytes
+    # two fp32 values per row, as two regions each padded to 256 bytes
+    assert fa.fa_bwd_workspace_size(2, 32, 4096, 128) == 2 * (2 * 32 * 4096 * 4)
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 64) == 2 * 256
     assert fa.fa_bwd_workspace_size(0, 1, 3, 64) == 0
     assert fa.fa_bwd_workspace_size(1, 1, 3, 80) == 0
 
