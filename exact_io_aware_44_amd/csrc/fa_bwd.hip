@@ -31,6 +31,8 @@
 // queries (dV^T = dO^T P, dK^T = Q^T dS); their A operands (dO^T, Q^T) are
 // transpose reads of the row-major LDS tiles.  The dq pass mirrors the
 // forward kernel (lane = query).
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -101,8 +103,8 @@ __global__ __launch_bounds__(256) void dsum_kernel(const bf16* o, const bf16* do
 
 // ---------------------------------------------------------------------------
 // 2. dK, dV: unit = (batch, head, 128-key tile); wave w owns keys 32w..32w+31
-//    of the tile and keeps their dK^T, dV^T accumulators in registers; K and V
-//    sit in LDS for the whole unit while 64-query stages of Q, dO,
+//    of the tile.  K and V (the B operands of S and dP) stay in VGPRs, the
+//    dK^T, dV^T accumulators in AGPRs, while 64-query stages of Q, dO,
 //    -L log2 e and D stream through double-buffered LDS.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -116,11 +118,6 @@ struct KvTile {
     static constexpr int RPL = 64 / CPR;           // rows per 1 KiB load
     static constexpr int DS = D / 16;              // MFMA k-steps across the head width
     static constexpr int DB = D / 32;              // 32-wide blocks of the head width
-    // K / V of the unit: row pitch padded by one chunk so the 16 rows a
-    // quarter-wave reads with ds_read_b128 land 4 banks apart
-    static constexpr int KSTR = D + 8;
-    static constexpr int KV_ELEMS = BK * KSTR;
-    static constexpr int KV_LOADS = BK * CPR / 64;  // 1 KiB loads per K or V tile
 };
 
 // Q / dO stages are stored with unpadded rows and the 16-byte chunk index of
@@ -138,6 +135,22 @@ __device__ __forceinline__ int qd_off(int r, int chunk) {  // element offset
     return r * D + ((chunk ^ qd_swz<D>(r)) << 3);
 }
 
+// acc += A * B on v_mfma_f32_32x32x16_bf16 with acc held in AGPRs (the
+// compiler would otherwise keep it in VGPRs, which this kernel needs for K, V
+// and the score tiles).  Hazards the compiler cannot see through the asm:
+//  - a VALU write of a or b needs two wait states before the MFMA reads it:
+//    the s_nop 1;
+//  - back-to-back accumulation into the same registers is interlocked;
+//  - reading acc after the last MFMA needs the wait of mfma_acc_drain.
+__device__ __forceinline__ void mfma_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last MFMA into an accumulator and any read of it
+// (a 16-pass MFMA result needs at most 18).
+__device__ __forceinline__ void mfma_acc_drain(f32x16& a, f32x16& b) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a), "+a"(b));
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     using T = KvTile<D>;
@@ -149,8 +162,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) bf16 do_lds1[T::T_ELEMS];
     __shared__ __attribute__((aligned(16))) float f_lds0[2 * T::BQ];  // -L log2 e, then D
     __shared__ __attribute__((aligned(16))) float f_lds1[2 * T::BQ];
-    __shared__ __attribute__((aligned(16))) bf16 k_lds[T::KV_ELEMS];
-    __shared__ __attribute__((aligned(16))) bf16 v_lds[T::KV_ELEMS];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -205,43 +216,51 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
         if (wave == 1) load4_lds(ddb, (uint32_t)(q0 + lane) * 4, fd + T::BQ);
     };
 
+    bf16x8 kreg[T::DS], vreg[T::DS];
     f32x16 dk[T::DB], dv[T::DB];
     int kw0 = 0, kj = 0;
 
-    // One 32-query block of a stage: S = Q K^T and dP = dO V^T (lane: key kj,
-    // local queries 8(r/4) + 4hi + r%4), P = exp2(S c - L log2 e),
-    // dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T
-    // delivered by transpose reads.
-    auto block = [&](const bf16* __restrict__ qs, const bf16* __restrict__ dos,
-                     const float* __restrict__ fs, int q0, int b)
-                     __attribute__((always_inline)) {
-        const int qb0 = q0 + 32 * b;
-        if (CAUSAL && qb0 + 31 < kw0) return;  // every query precedes our keys
-        f32x16 s = f32x16{}, dp = f32x16{};
+    // S = Q K^T and dP = dO V^T for the 32-query block b of a stage; lane:
+    // key kj, local queries 32b + 8(r/4) + 4hi + r%4 (register r).
+    auto scores = [&](const bf16* __restrict__ qs, const bf16* __restrict__ dos, int b,
+                      f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+        s = f32x16{};
+        dp = f32x16{};
 #pragma unroll
         for (int ss = 0; ss < T::DS; ++ss) {
             const int off = qd_off<D>(32 * b + l32, 2 * ss + hi);
-            const int koff = (32 * wave + l32) * T::KSTR + 16 * ss + 8 * hi;
-            s = mfma32(lds_read16(qs + off), lds_read16(k_lds + koff), s);
-            dp = mfma32(lds_read16(dos + off), lds_read16(v_lds + koff), dp);
+            s = mfma32(lds_read16(qs + off), kreg[ss], s);
+            dp = mfma32(lds_read16(dos + off), vreg[ss], dp);
         }
-        const bool need_mask = CAUSAL && qb0 < kw0 + 31;
+    };
+    // P = exp2(S c - L log2 e) and dS = P (dP - D), rounded to bf16 in the
+    // B-operand order of the two 16-query k-steps; MASK zeroes the weights
+    // of keys after their query (tiles on the causal diagonal only).
+    auto weights = [&](const float* __restrict__ fs, int qb0, int b, const f32x16& s,
+                       const f32x16& dp, bf16x8* pb, bf16x8* sb, auto mask_tag)
+                       __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const int tm = kj - qb0 - 4 * hi;  // masked where tm > local query offset
-        bf16x8 pb[2], sb[2];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             const f32x4 nl = *reinterpret_cast<const f32x4*>(fs + 32 * b + 8 * a + 4 * hi);
-            const f32x4 dd = *reinterpret_cast<const f32x4*>(fs + T::BQ + 32 * b + 8 * a + 4 * hi);
+            const f32x4 dd =
+                *reinterpret_cast<const f32x4*>(fs + T::BQ + 32 * b + 8 * a + 4 * hi);
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int r = 4 * a + x;
                 float pv = exp2_fast(__builtin_fmaf(s[r], p.c, nl[x]));
-                if (need_mask) pv = tm > 8 * a + x ? 0.f : pv;
+                if (MASK) pv = tm > 8 * a + x ? 0.f : pv;
                 const float dsv = pv * (dp[r] - dd[x]);
                 pb[r / 8][r % 8] = to_bf16(pv);
                 sb[r / 8][r % 8] = to_bf16(dsv);
             }
         }
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T by transpose reads,
+    // their query order matching the B operands'.
+    auto accumulate = [&](const bf16* __restrict__ qs, const bf16* __restrict__ dos, int b,
+                          const bf16x8* pb, const bf16x8* sb) __attribute__((always_inline)) {
 #pragma unroll
         for (int e = 0; e < T::DB; ++e)
 #pragma unroll
@@ -251,23 +270,56 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
                 const int o0 = qd_off<D>(rr, cc) + 4 * (i16 & 1);
                 const int o1 = qd_off<D>(rr + 8, cc) + 4 * (i16 & 1);
                 const bf16x8 doT = cat(lds_read_tr(dos + o0), lds_read_tr(dos + o1));
-                dv[e] = mfma32(doT, pb[t], dv[e]);
+                mfma_acc(dv[e], doT, pb[t]);
                 const bf16x8 qT = cat(lds_read_tr(qs + o0), lds_read_tr(qs + o1));
-                dk[e] = mfma32(qT, sb[t], dk[e]);
+                mfma_acc(dk[e], qT, sb[t]);
             }
     };
+    using True = std::true_type;
+    using False = std::false_type;
+
+    // One 64-query stage.  MASKED: a stage on the causal diagonal of this
+    // wave's keys (blocks wholly before the keys are skipped, the rest
+    // masked); otherwise both blocks run straight through, block 1's products
+    // issued before block 0's weights so the matrix unit stays busy while the
+    // exponentials run.
     auto step = [&](int qt, bool more, const bf16* __restrict__ qs,
                     const bf16* __restrict__ dos, const float* __restrict__ fs,
-                    bf16* __restrict__ qn, bf16* __restrict__ don, float* __restrict__ fn)
-                    __attribute__((always_inline)) {
+                    bf16* __restrict__ qn, bf16* __restrict__ don, float* __restrict__ fn,
+                    auto mask_tag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(mask_tag)::value;
         if (more) load_stage((qt + 1) * T::BQ, qn, don, fn);
-        block(qs, dos, fs, qt * T::BQ, 0);
-        // keep the two blocks apart: interleaving them would need more
-        // registers than a wave has
-        __builtin_amdgcn_sched_barrier(0);
-        block(qs, dos, fs, qt * T::BQ, 1);
+        const int q0 = qt * T::BQ;
+        f32x16 s0, dp0;
+        bf16x8 pb0[2], sb0[2];
+        if constexpr (!MASKED) {
+            f32x16 s1, dp1;
+            bf16x8 pb1[2], sb1[2];
+            scores(qs, dos, 0, s0, dp0);
+            scores(qs, dos, 1, s1, dp1);
+            weights(fs, q0, 0, s0, dp0, pb0, sb0, False{});
+            accumulate(qs, dos, 0, pb0, sb0);
+            weights(fs, q0 + 32, 1, s1, dp1, pb1, sb1, False{});
+            accumulate(qs, dos, 1, pb1, sb1);
+        } else {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int qb0 = q0 + 32 * b;
+                if (qb0 + 31 < kw0) continue;  // every query precedes our keys
+                scores(qs, dos, b, s0, dp0);
+                weights(fs, qb0, b, s0, dp0, pb0, sb0, True{});
+                accumulate(qs, dos, b, pb0, sb0);
+            }
+        }
         wait_vmem_lds();  // next stage landed; this stage's reads are done
         barrier_only();
+    };
+    auto run_stage = [&](int qt, int qt_begin, int nqt, auto mask_tag)
+                         __attribute__((always_inline)) {
+        const bool more = qt + 1 < nqt;
+        const bool odd = (qt - qt_begin) & 1;
+        step(qt, more, odd ? q_lds1 : q_lds0, odd ? do_lds1 : do_lds0, odd ? f_lds1 : f_lds0,
+             odd ? q_lds0 : q_lds1, odd ? do_lds0 : do_lds1, odd ? f_lds0 : f_lds1, mask_tag);
     };
 
     for (int rep = 0; rep < 2; ++rep) {
@@ -276,15 +328,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
         const int k0u = kt * T::BK;
         kw0 = k0u + 32 * wave;
         kj = kw0 + l32;
-        // K and V of the tile into LDS (rows padded to KSTR): the padded
-        // layout is not contiguous, so these go through registers
 #pragma unroll
-        for (int x = 0; x < T::KV_LOADS / 4; ++x) {
-            const int c = 64 * (wave + 4 * x) + lane;  // chunk index in the tile
-            const int r = c / T::CPR, cc = c % T::CPR;
-            const uint32_t off = ((uint32_t)(k0u + r) * D + cc * 8) * 2;
-            lds_write16(k_lds + r * T::KSTR + cc * 8, load16(kb, off));
-            lds_write16(v_lds + r * T::KSTR + cc * 8, load16(vb, off));
+        for (int s = 0; s < T::DS; ++s) {
+            const uint32_t off = ((uint32_t)kj * D + 16 * s + 8 * hi) * 2;
+            kreg[s] = __builtin_bit_cast(bf16x8, load16(kb, off));
+            vreg[s] = __builtin_bit_cast(bf16x8, load16(vb, off));
         }
 #pragma unroll
         for (int e = 0; e < T::DB; ++e) {
@@ -297,13 +345,18 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
         load_stage(qt_begin * T::BQ, q_lds0, do_lds0, f_lds0);
         wait_vmem_lds();
         barrier_only();
-        for (int qt = qt_begin; qt < nqt; ++qt) {
-            const bool more = qt + 1 < nqt;
-            const bool odd = (qt - qt_begin) & 1;
-            step(qt, more, odd ? q_lds1 : q_lds0, odd ? do_lds1 : do_lds0,
-                 odd ? f_lds1 : f_lds0, odd ? q_lds0 : q_lds1, odd ? do_lds0 : do_lds1,
-                 odd ? f_lds0 : f_lds1);
+        // The first two stages hold the diagonal of every wave's keys (a
+        // wave's 32 keys start at most 96 past the tile start); separate
+        // loops keep the straight-line interior loop free of the masked
+        // variant, and the accumulators in one register assignment.
+        int qt = qt_begin;
+        if (CAUSAL) {
+            const int diag_end = min(nqt, qt_begin + 2);
+            for (; qt < diag_end; ++qt) run_stage(qt, qt_begin, nqt, True{});
         }
+        for (; qt < nqt; ++qt) run_stage(qt, qt_begin, nqt, False{});
+#pragma unroll
+        for (int e = 0; e < T::DB; ++e) mfma_acc_drain(dv[e], dk[e]);
         // dV[kj][d], dK[kj][d] = scale * acc (d = 32e + 8(r/4) + 4hi + r%4)
 #pragma unroll
         for (int e = 0; e < T::DB; ++e)
@@ -321,34 +374,54 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ: unit = (batch, head, 128-query tile); 4 waves x 32 queries.
+// 3. dQ: unit = (batch, head, 128-query tile); wave w owns queries
+//    32w..32w+31 of the tile and keeps them (Q, dO as B operands) in VGPRs
+//    and their dQ^T accumulator in AGPRs while 64-key stages of K and V
+//    stream through double-buffered LDS.  Scores are taken transposed,
+//    S^T = K Q^T, so each lane holds one query and its L and D are scalars.
 // ---------------------------------------------------------------------------
 template <int D>
 struct QTile {
-    static constexpr int BR = 128;
-    static constexpr int BC = 64;
+    static constexpr int BR = 128;                 // queries per unit
+    static constexpr int BC = 64;                  // keys per streamed stage
     static constexpr int THREADS = 256;
-    static constexpr int KSTR = D + 8;
-    static constexpr int K_ELEMS = BC * KSTR;
-    static constexpr int STAGE = 2 * K_ELEMS;  // K then V
-    static constexpr int CPT = BC * D / 8 / THREADS;
+    static constexpr int CPR = D / 8;
+    static constexpr int T_ELEMS = BC * D;         // one K or V stage
+    static constexpr int LPW = BC * CPR / 64 / 4;  // 1 KiB loads per wave per tile
+    static constexpr int RPL = 64 / CPR;
     static constexpr int DS = D / 16;
     static constexpr int DB = D / 32;
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p, int n_qt) {
+__global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     using T = QTile<D>;
-    __shared__ __attribute__((aligned(16))) bf16 lds[2 * T::STAGE];
+    __shared__ __attribute__((aligned(16))) bf16 k_lds0[T::T_ELEMS];
+    __shared__ __attribute__((aligned(16))) bf16 k_lds1[T::T_ELEMS];
+    __shared__ __attribute__((aligned(16))) bf16 v_lds0[T::T_ELEMS];
+    __shared__ __attribute__((aligned(16))) bf16 v_lds1[T::T_ELEMS];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5;
     const int g = lane >> 4, i16 = lane & 15;
-    const int qt = CAUSAL ? (n_qt - 1 - (int)blockIdx.x) : (int)blockIdx.x;
-    const int h = blockIdx.y, b = blockIdx.z;
+    int head, uidx;
+    unit_of(blockIdx.x, gridDim.x, p.per_head, head, uidx);
     const int n = p.N;
-    const int q0 = qt * T::BR;
-    const int64_t row0 = ((int64_t)b * p.H + h) * n;
+    const int nqt = (n + T::BR - 1) / T::BR;
+    // query tiles of this unit: under causal masking a heavy one (late, many
+    // keys) and the matching light one
+    int t0 = uidx, t1 = -1;
+    if (CAUSAL) {
+        t0 = nqt - 1 - uidx;
+        t1 = uidx;
+        if (t1 > t0) return;
+        if (t1 == t0) t1 = -1;
+    } else if (t0 >= nqt) {
+        return;
+    }
+
+    const int64_t row0 = (int64_t)head * n;
     const uint32_t bytes = (uint32_t)n * D * 2;
     const Buf qb = make_buf(p.q + row0 * D, bytes);
     const Buf kb = make_buf(p.k + row0 * D, bytes);
@@ -358,114 +431,160 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p, int n_qt) {
     const Buf ddb = make_buf(p.dd + row0, (uint32_t)n * 4);
     const Buf dqb = make_buf(p.dq + row0 * D, bytes);
 
-    const int qw0 = q0 + 32 * wave;
-    const int qi = qw0 + l32;
+    uint32_t koff[T::LPW];
+#pragma unroll
+    for (int x = 0; x < T::LPW; ++x) {
+        const int L = wave * T::LPW + x;
+        const int r = L * T::RPL + lane / T::CPR;
+        const int pc = lane % T::CPR;
+        koff[x] = (uint32_t)(r * D + ((pc ^ qd_swz<D>(r)) << 3)) * 2;
+    }
+    auto load_stage = [&](int k0, bf16* __restrict__ kd, bf16* __restrict__ vd)
+                          __attribute__((always_inline)) {
+#pragma unroll
+        for (int x = 0; x < T::LPW; ++x) {
+            const int L = wave * T::LPW + x;
+            load16_lds(kb, koff[x] + (uint32_t)k0 * D * 2, kd + 512 * L);
+            load16_lds(vb, koff[x] + (uint32_t)k0 * D * 2, vd + 512 * L);
+        }
+    };
 
     bf16x8 qreg[T::DS], doreg[T::DS];
-#pragma unroll
-    for (int s = 0; s < T::DS; ++s) {
-        const uint32_t off = ((uint32_t)qi * D + 16 * s + 8 * hi) * 2;
-        qreg[s] = __builtin_bit_cast(bf16x8, load16(qb, off));
-        doreg[s] = __builtin_bit_cast(bf16x8, load16(dob, off));
-    }
-    const float nl2 = loadf(nlb, (uint32_t)qi * 4);
-    const float dd = loadf(ddb, (uint32_t)qi * 4);
-
-    const int kend = CAUSAL ? min(n, q0 + T::BR) : n;
-    const int nkt = (kend + T::BC - 1) / T::BC;
-
     f32x16 acc[T::DB];
-#pragma unroll
-    for (int e = 0; e < T::DB; ++e) acc[e] = f32x16{};
+    int qi = 0;
+    float nl2 = 0.f, dd = 0.f;
 
-    u32x4 kreg_g[T::CPT], vreg_g[T::CPT];
-    auto gload = [&](int k0) {
+    // S^T = K Q^T and dP^T = V dO^T for the 32-key block b of a stage; lane:
+    // query qi, local keys 32b + 8(r/4) + 4hi + r%4 (register r).
+    auto scores = [&](const bf16* __restrict__ ks, const bf16* __restrict__ vs, int b,
+                      f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+        s = f32x16{};
+        dp = f32x16{};
 #pragma unroll
-        for (int i = 0; i < T::CPT; ++i) {
-            const int c = tid + T::THREADS * i;
-            const int r = c / (D / 8), cc = c % (D / 8);
-            const uint32_t off = ((uint32_t)(k0 + r) * D + cc * 8) * 2;
-            kreg_g[i] = load16(kb, off);
-            vreg_g[i] = load16(vb, off);
+        for (int ss = 0; ss < T::DS; ++ss) {
+            const int off = qd_off<D>(32 * b + l32, 2 * ss + hi);
+            s = mfma32(lds_read16(ks + off), qreg[ss], s);
+            dp = mfma32(lds_read16(vs + off), doreg[ss], dp);
         }
     };
-    auto lstore = [&](int stage) {
-        bf16* ks = lds + stage * T::STAGE;
-        bf16* vs = ks + T::K_ELEMS;
+    // dS^T = P^T (dP^T - D), P^T = exp2(S^T c - L log2 e), in bf16 B-operand
+    // order; MASK zeroes the weights of keys after the lane's query.
+    auto weights = [&](int kb0, const f32x16& s, const f32x16& dp, bf16x8* sb,
+                       auto mask_tag) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const int lim = qi - kb0 - 4 * hi;  // masked where local key offset > lim
 #pragma unroll
-        for (int i = 0; i < T::CPT; ++i) {
-            const int c = tid + T::THREADS * i;
-            const int r = c / (D / 8), cc = c % (D / 8);
-            lds_write16(ks + r * T::KSTR + cc * 8, kreg_g[i]);
-            lds_write16(vs + r * T::KSTR + cc * 8, vreg_g[i]);
+        for (int r = 0; r < 16; ++r) {
+            float pv = exp2_fast(__builtin_fmaf(s[r], p.c, nl2));
+            if (MASK) pv = 8 * (r >> 2) + (r & 3) > lim ? 0.f : pv;
+            sb[r / 8][r % 8] = to_bf16(pv * (dp[r] - dd));
         }
     };
-    auto compute = [&](int stage, int k0) {
-        if (CAUSAL && k0 > qw0 + 31) return;
-        const bf16* ks = lds + stage * T::STAGE;
-        const bf16* vs = ks + T::K_ELEMS;
-        // S^T and dP^T: lane holds query qi, keys k0 + 32bb + 8(r/4) + 4hi + r%4
-        f32x16 s[2], dp[2];
+    // dQ^T += K^T dS^T with K^T by transpose reads of the row-major stage.
+    auto accumulate = [&](const bf16* __restrict__ ks, int b, const bf16x8* sb)
+                          __attribute__((always_inline)) {
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            s[bb] = f32x16{};
-            dp[bb] = f32x16{};
+        for (int e = 0; e < T::DB; ++e)
 #pragma unroll
-            for (int ss = 0; ss < T::DS; ++ss) {
-                const int off = (32 * bb + l32) * T::KSTR + 16 * ss + 8 * hi;
-                s[bb] = mfma32(lds_read16(ks + off), qreg[ss], s[bb]);
-                dp[bb] = mfma32(lds_read16(vs + off), doreg[ss], dp[bb]);
+            for (int t = 0; t < 2; ++t) {
+                const int rr = 32 * b + 16 * t + 4 * hi + (i16 >> 2);
+                const int cc = 4 * e + 2 * (g & 1) + ((i16 & 3) >> 1);
+                const int o0 = qd_off<D>(rr, cc) + 4 * (i16 & 1);
+                const int o1 = qd_off<D>(rr + 8, cc) + 4 * (i16 & 1);
+                mfma_acc(acc[e], cat(lds_read_tr(ks + o0), lds_read_tr(ks + o1)), sb[t]);
+            }
+    };
+    using True = std::true_type;
+    using False = std::false_type;
+
+    // One 64-key stage.  MASKED: a stage on the causal diagonal (blocks
+    // wholly after this wave's queries skipped, the rest masked).
+    auto step = [&](int ks_i, bool more, const bf16* __restrict__ ks,
+                    const bf16* __restrict__ vs, bf16* __restrict__ kn,
+                    bf16* __restrict__ vn, int qw0, auto mask_tag)
+                    __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(mask_tag)::value;
+        if (more) load_stage((ks_i + 1) * T::BC, kn, vn);
+        const int k0 = ks_i * T::BC;
+        f32x16 s0, dp0;
+        bf16x8 sb0[2];
+        if constexpr (!MASKED) {
+            f32x16 s1, dp1;
+            bf16x8 sb1[2];
+            // two workgroups per CU interleave one wave's matrix products
+            // with the other's exponentials; keeping the blocks apart keeps
+            // the registers within that occupancy
+            scores(ks, vs, 0, s0, dp0);
+            weights(k0, s0, dp0, sb0, False{});
+            accumulate(ks, 0, sb0);
+            __builtin_amdgcn_sched_barrier(0);
+            scores(ks, vs, 1, s1, dp1);
+            weights(k0 + 32, s1, dp1, sb1, False{});
+            accumulate(ks, 1, sb1);
+        } else {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int kb0 = k0 + 32 * b;
+                if (kb0 > qw0 + 31) continue;  // every key follows our queries
+                scores(ks, vs, b, s0, dp0);
+                weights(kb0, s0, dp0, sb0, True{});
+                accumulate(ks, b, sb0);
             }
         }
-        const bool need_mask = (CAUSAL && k0 + T::BC - 1 > qw0) || (k0 + T::BC > n);
-        bf16x8 sb[2][2];
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float pv = exp2_fast(__builtin_fmaf(s[bb][r], p.c, nl2));
-                if (need_mask) {
-                    const int key = k0 + 32 * bb + 8 * (r / 4) + 4 * hi + (r & 3);
-                    if ((CAUSAL && key > qi) || key >= n) pv = 0.f;
-                }
-                sb[bb][r / 8][r % 8] = to_bf16(pv * (dp[bb][r] - dd));
-            }
-        // dQ^T += K^T dS^T (K^T by transpose reads of row-major K)
-#pragma unroll
-        for (int e = 0; e < T::DB; ++e) {
-            const int dcol = 32 * e + 16 * (g & 1) + 4 * (i16 & 3);
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int kr = 32 * bb + 16 * t + 4 * hi + (i16 >> 2);
-                    const bf16x8 kT = cat(lds_read_tr(ks + kr * T::KSTR + dcol),
-                                          lds_read_tr(ks + (kr + 8) * T::KSTR + dcol));
-                    acc[e] = mfma32(kT, sb[bb][t], acc[e]);
-                }
-        }
+        wait_vmem_lds();
+        barrier_only();
+    };
+    auto run_stage = [&](int ks_i, int nks, int qw0, auto mask_tag)
+                         __attribute__((always_inline)) {
+        const bool more = ks_i + 1 < nks;
+        const bool odd = ks_i & 1;
+        step(ks_i, more, odd ? k_lds1 : k_lds0, odd ? v_lds1 : v_lds0, odd ? k_lds0 : k_lds1,
+             odd ? v_lds0 : v_lds1, qw0, mask_tag);
     };
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nkt; ++kt) {
-        const bool more = kt + 1 < nkt;
-        if (more) gload((kt + 1) * T::BC);
-        compute(kt & 1, kt * T::BC);
-        if (more) lstore((kt + 1) & 1);
-        __syncthreads();
+    for (int rep = 0; rep < 2; ++rep) {
+        const int qt = rep == 0 ? t0 : t1;
+        if (qt < 0) break;
+        const int q0 = qt * T::BR;
+        const int qw0 = q0 + 32 * wave;
+        qi = qw0 + l32;
+#pragma unroll
+        for (int s = 0; s < T::DS; ++s) {
+            const uint32_t off = ((uint32_t)qi * D + 16 * s + 8 * hi) * 2;
+            qreg[s] = __builtin_bit_cast(bf16x8, load16(qb, off));
+            doreg[s] = __builtin_bit_cast(bf16x8, load16(dob, off));
+        }
+        nl2 = loadf(nlb, (uint32_t)qi * 4);
+        dd = loadf(ddb, (uint32_t)qi * 4);
+#pragma unroll
+        for (int e = 0; e < T::DB; ++e) acc[e] = f32x16{};
+
+        // key stages: causal units stop at the tile's last query; the last
+        // two stages (keys q0 .. q0+127) are the diagonal
+        const int kend = CAUSAL ? min(n, q0 + T::BR) : n;
+        const int nks = (kend + T::BC - 1) / T::BC;
+        const int n_plain = CAUSAL ? max(0, min(nks, q0 / T::BC)) : nks;
+        load_stage(0, k_lds0, v_lds0);
+        wait_vmem_lds();
+        barrier_only();
+        int ks_i = 0;
+        for (; ks_i < n_plain; ++ks_i) run_stage(ks_i, nks, qw0, False{});
+        if (CAUSAL)
+            for (; ks_i < nks; ++ks_i) run_stage(ks_i, nks, qw0, True{});
+
+#pragma unroll
+        for (int e = 0; e < T::DB; e += 2) mfma_acc_drain(acc[e], acc[e + 1]);
+        // dQ[qi][d] = scale * acc (d = 32e + 8(r/4) + 4hi + r%4)
+#pragma unroll
+        for (int e = 0; e < T::DB; ++e)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = 32 * e + 8 * r4 + 4 * hi;
+                store8(dqb, ((uint32_t)qi * D + d) * 2,
+                       pack4(acc[e][4 * r4] * p.scale, acc[e][4 * r4 + 1] * p.scale,
+                             acc[e][4 * r4 + 2] * p.scale, acc[e][4 * r4 + 3] * p.scale));
+            }
     }
-
-#pragma unroll
-    for (int e = 0; e < T::DB; ++e)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int d = 32 * e + 8 * r4 + 4 * hi;
-            store8(dqb, ((uint32_t)qi * D + d) * 2,
-                   pack4(acc[e][4 * r4] * p.scale, acc[e][4 * r4 + 1] * p.scale,
-                         acc[e][4 * r4 + 2] * p.scale, acc[e][4 * r4 + 3] * p.scale));
-        }
 }
 
 template <int D, bool CAUSAL>
@@ -502,9 +621,12 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream) {
     err = hipGetLastError();
     if (err != hipSuccess) return err;
 
+    // the dQ pass: per_head query tiles (pairs under causal masking)
     const int nqt = (a.N + QTile<D>::BR - 1) / QTile<D>::BR;
-    hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(nqt, a.H, a.B), dim3(256), 0,
-                       stream, p, nqt);
+    p.per_head = CAUSAL ? (nqt + 1) / 2 : nqt;
+    const int64_t qunits = (int64_t)p.per_head * a.H * a.B;
+    hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3((unsigned)qunits), dim3(256), 0, stream,
+                       p);
     return hipGetLastError();
 }
 
