@@ -215,6 +215,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int e = 0; e < T::DB; ++e) acc[e] = f32x16{};
     float m_run = kNegInf, l_run = 0.f;  // l_run: this lane's half of the keys
+    float l_new = 0.f;                     // sum of the latest half's weights
 
     // ---- the pipeline works on 32-key half tiles: half h holds keys
     //      32h .. 32h+31 (LDS tile h/2, rows 32*(h%2) ..).  Its scores live in
@@ -247,27 +248,34 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         upd = mx > m_run + kLazyRescale;  // the first live half always moves it
         const float m_new = upd ? mx : m_run;
         const float m_use = (m_new == kNegInf) ? 0.f : m_new;  // no key yet: no NaN
-        alpha = upd ? exp2_fast(m_run - m_use) : 1.f;
+        alpha = m_run - m_use;  // log2 of the rescale factor: 0 unless upd
         m_run = m_new;
         // exponentials in place, summed in fp32 in four independent chains
         // (summing the bf16-rounded weights instead would put up to 2^-9
         // relative error into l when one weight dominates and the reference
         // maximum is stale), then packed to bf16
-        float rs[4] = {0.f, 0.f, 0.f, 0.f};
+        float rs[4];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             s[r] = exp2_fast(__builtin_fmaf(s[r], p.c, -m_use));
-            rs[r & 3] += s[r];
+            rs[r & 3] = r < 4 ? s[r] : rs[r & 3] + s[r];
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = to_bf16(s[r]);
-        l_run = __builtin_fmaf(l_run, alpha, (rs[0] + rs[1]) + (rs[2] + rs[3]));
+        l_new = (rs[0] + rs[1]) + (rs[2] + rs[3]);  // taken against m_new
     };
+    // Bring the old sums (u, and l before this half) to the new maximum, then
+    // add this half's sum.  alpha is the log2 factor m_old - m_new, 0 on lanes
+    // whose maximum did not move, so the exponential and the multiplies run
+    // only when some lane moved.
     auto rescale = [&](float alpha, bool upd) {
         if (__any(upd)) {
+            const float f = exp2_fast(alpha);
 #pragma unroll
-            for (int e = 0; e < T::DB; ++e) acc[e] *= alpha;
+            for (int e = 0; e < T::DB; ++e) acc[e] *= f;
+            l_run *= f;
         }
+        l_run += l_new;
     };
 
     // MFMA operands.  S: A = K rows (ds_read_b128), B = Q registers.  P.V:
@@ -313,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
             }
         };
         if constexpr (DO_S) s_nxt = f32x16{};
-        constexpr int PF = 4;  // operand read distance, in MFMAs
+        constexpr int PF = 6;  // operand read distance, in MFMAs
         bf16x8 op[NM > 0 ? NM : 1];
 #pragma unroll
         for (int i = 0; i < PF && i < NM; ++i) op[i] = fetch(i);
@@ -341,6 +349,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     for (int ss = 0; ss < T::DS; ++ss) sA = mfma32(k_op(k_lds0, 0, ss), qreg[ss], sA);
     if (needs_mask(0)) apply_mask(sA, 0);
     half_step(True{}, False{}, True{}, k_lds0, 1, nullptr, 0, sA, sB, pB, pA, alpha, upd);
+    l_run = l_new;  // first half: nothing to rescale
     __syncthreads();  // K_0 is consumed before tile-step 0 reloads its buffer
 
     // ---- tile-steps.  Tile-step j runs half-steps 2j+1 (odd: softmax sB ->
