@@ -65,9 +65,15 @@ def _load():
     lib.oracle_attn_fwd_varlen_rows.argtypes = [
         _D, _D, _D, _I32, _i64, _i64, _i64, _i64, ctypes.c_double,
         ctypes.c_int, _I64, _I64, _i64, _D, _D]
+    lib.oracle_attn_fwd_qk.argtypes = [_D, _D, _D, _D, _D, _i64, _i64, _i64,
+                                       _i64, _i64, ctypes.c_double, ctypes.c_int]
+    lib.oracle_attn_fwd_qk_rows.argtypes = [_D, _D, _D, _I64, _I64, _i64, _D, _D,
+                                            _i64, _i64, _i64, _i64, _i64,
+                                            ctypes.c_double, ctypes.c_int]
     lib.oracle_attn_bwd.argtypes = [_D, _D, _D, _D, _D, _D, _D, _i64, _i64,
                                     _i64, _i64, ctypes.c_double, ctypes.c_int]
     for f in (lib.oracle_attn_fwd, lib.oracle_attn_fwd_rows,
+              lib.oracle_attn_fwd_qk, lib.oracle_attn_fwd_qk_rows,
               lib.oracle_attn_fwd_varlen, lib.oracle_attn_fwd_varlen_rows,
               lib.oracle_attn_bwd):
         f.restype = ctypes.c_int
@@ -127,6 +133,41 @@ def fwd_rows(q, k, v, scale: float, causal: bool, bh, rows):
                                         _p(rows, _I64), n, _p(o), _p(lse), B,
                                         H, N, D, float(scale),
                                         int(bool(causal))), "fwd_rows")
+    return o, lse
+
+
+def fwd_qk(q, k, v, scale: float, causal: bool):
+    """Nq queries against Nk keys.  q: [B, H, Nq, D]; k, v: [B, H, Nk, D].
+
+    Under the causal mask query i reads keys j <= i + Nk - Nq (bottom-right
+    alignment).  Returns (O [B,H,Nq,D], L [B,H,Nq]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    assert k.shape == (B, H, Nk, D) and v.shape == k.shape
+    o = np.empty_like(q)
+    lse = np.empty((B, H, Nq), dtype=np.float64)
+    _check(_load().oracle_attn_fwd_qk(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H,
+                                      Nq, Nk, D, float(scale), int(bool(causal))),
+           "fwd_qk")
+    return o, lse
+
+
+def fwd_qk_rows(q, k, v, scale: float, causal: bool, bh, rows):
+    """Selected rows of fwd_qk (bh[t] = b*H + h, rows[t] the query row)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    bh = np.ascontiguousarray(bh, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    n = bh.shape[0]
+    o = np.empty((n, D), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    _check(_load().oracle_attn_fwd_qk_rows(_p(q), _p(k), _p(v), _p(bh, _I64),
+                                           _p(rows, _I64), n, _p(o), _p(lse), B, H,
+                                           Nq, Nk, D, float(scale), int(bool(causal))),
+           "fwd_qk_rows")
     return o, lse
 
 

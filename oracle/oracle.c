@@ -31,8 +31,14 @@
  *  - causal allows j <= i (a token may read itself);
  *  - the scale is applied to the dot product, in fp64 here;
  *  - L uses the natural logarithm, in units of scaled scores;
- *  - a row with no allowed key (never reached by the supported shapes) gets
- *    O = 0 and L = -inf;
+ *  - a row with no allowed key gets O = 0 and L = -inf (reached only when
+ *    there are more queries than keys under the bottom-right causal mask);
+ *  - queries and keys of different lengths (tensortonic section 9 warns that
+ *    the square causal mask is not right for every unequal-length layout):
+ *    the queries are the last Nq positions of a sequence whose keys are all
+ *    Nk positions, so query i sits at position i + Nk - Nq and, under the
+ *    causal mask, reads keys j <= i + Nk - Nq (the mask aligned bottom-right;
+ *    for Nq = Nk it is the square mask);
  *  - the backward pass is the exact vector-Jacobian product of this forward
  *    map (the pages give only "weight = exp(s_ij - L_i)" and that each tile
  *    contributes to dQ, dK and dV): with dP_ij = <dO_i, v_j> and
@@ -163,6 +169,75 @@ int oracle_attn_fwd_rows(const double* q, const double* k, const double* v,
                 attend_row(q + base + i * D, k + base, v + base,
                            allowed_keys(i, N, causal), D, scale, s,
                            o_rows + t * D, lse_rows + t);
+            }
+            free(s);
+        }
+    }
+    return fail;
+}
+
+/*
+ * Keys row i of Nq queries may read out of Nk: all of them, or under the
+ * causal mask those at positions <= i + Nk - Nq (bottom-right alignment).
+ */
+static int64_t allowed_keys_qk(int64_t i, int64_t nq, int64_t nk, int causal) {
+    if (!causal) return nk;
+    const int64_t last = i + nk - nq;  /* last readable key position */
+    return last < 0 ? 0 : (last + 1 < nk ? last + 1 : nk);
+}
+
+/*
+ * Forward with Nq queries against Nk keys: q, o are [B, H, Nq, D], k, v are
+ * [B, H, Nk, D], lse is [B, H, Nq].
+ */
+int oracle_attn_fwd_qk(const double* q, const double* k, const double* v,
+                       double* o, double* lse, int64_t B, int64_t H, int64_t Nq,
+                       int64_t Nk, int64_t D, double scale, int causal) {
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || D <= 0) return 1;
+    const int64_t rows = B * H * Nq;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < rows; ++r) {
+                const int64_t bh = r / Nq, i = r % Nq;
+                attend_row(q + (bh * Nq + i) * D, k + bh * Nk * D, v + bh * Nk * D,
+                           allowed_keys_qk(i, Nq, Nk, causal), D, scale, s,
+                           o + (bh * Nq + i) * D, lse + bh * Nq + i);
+            }
+            free(s);
+        }
+    }
+    return fail;
+}
+
+/* Selected rows of oracle_attn_fwd_qk (head bh[t] = b*H + h, query row[t]). */
+int oracle_attn_fwd_qk_rows(const double* q, const double* k, const double* v,
+                            const int64_t* bh, const int64_t* row, int64_t nrows,
+                            double* o_rows, double* lse_rows, int64_t B, int64_t H,
+                            int64_t Nq, int64_t Nk, int64_t D, double scale,
+                            int causal) {
+    for (int64_t t = 0; t < nrows; ++t)
+        if (bh[t] < 0 || bh[t] >= B * H || row[t] < 0 || row[t] >= Nq) return 2;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t t = 0; t < nrows; ++t) {
+                const int64_t i = row[t];
+                attend_row(q + (bh[t] * Nq + i) * D, k + bh[t] * Nk * D,
+                           v + bh[t] * Nk * D, allowed_keys_qk(i, Nq, Nk, causal), D,
+                           scale, s, o_rows + t * D, lse_rows + t);
             }
             free(s);
         }

@@ -371,3 +371,94 @@ def test_input_generators_are_seeded_bf16():
     assert len(lengths) == 16 and all(128 <= n <= 8192 for n in lengths)
     cu = attn_inputs.cu_seqlens(lengths)
     assert cu.dtype == torch.int32 and int(cu[-1]) == sum(lengths)
+
+
+# --------------------------------------------------------------------------
+# Unequal query and key lengths.  The square causal mask is not right for
+# every unequal-length layout (tensortonic section 9); the queries are the
+# last Nq positions of the key sequence, so the mask is aligned bottom-right.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk", [(1, 37), (5, 64), (64, 17), (33, 33), (100, 260)])
+def test_unequal_lengths_match_torch_sdpa_with_explicit_mask(Nq, Nk, causal):
+    g = torch.Generator().manual_seed(Nq * 1000 + Nk)
+    D = 16
+    q = torch.randn(2, 3, Nq, D, generator=g, dtype=torch.float64)
+    k, v = (torch.randn(2, 3, Nk, D, generator=g, dtype=torch.float64) for _ in range(2))
+    scale = 0.3
+    o, lse = oracle.fwd_qk(q, k, v, scale, causal)
+    mask = torch.ones(Nq, Nk, dtype=torch.bool)
+    if causal:
+        mask = mask.tril(diagonal=Nk - Nq)  # query i reads keys j <= i + Nk - Nq
+    live = mask.any(dim=1).numpy()
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, attn_mask=mask, scale=scale).numpy()
+    assert np.abs(o[:, :, live] - ref[:, :, live]).max() < 1e-12
+    s = scale * (q @ k.transpose(-1, -2))
+    ref_l = torch.logsumexp(s.masked_fill(~mask, -math.inf), dim=-1).numpy()
+    assert np.abs(lse[:, :, live] - ref_l[:, :, live]).max() < 1e-12
+    # rows with no readable key (more queries than keys under the causal mask)
+    assert (o[:, :, ~live] == 0).all() and np.isneginf(lse[:, :, ~live]).all()
+    assert live.all() == (not causal or Nq <= Nk)
+
+
+def test_unequal_lengths_special_cases():
+    q, k, v = (_rand(s, seed) for s, seed in (((2, 2, 9, 8), 30), ((2, 2, 9, 8), 31),
+                                               ((2, 2, 9, 8), 32)))
+    for causal in (False, True):  # equal lengths: the square definition
+        a = oracle.fwd_qk(q, k, v, 0.4, causal)
+        b = oracle.fwd(q, k, v, 0.4, causal)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    kl, vl = _rand((2, 2, 40, 8), 33), _rand((2, 2, 40, 8), 34)
+    oc, lc = oracle.fwd_qk(q, kl, vl, 0.4, True)
+    on, ln = oracle.fwd_qk(q, kl, vl, 0.4, False)
+    # the last query reads every key; one query alone (decoding) reads them all
+    assert np.abs(oc[:, :, -1] - on[:, :, -1]).max() < 1e-15
+    o1, l1 = oracle.fwd_qk(q[:, :, -1:], kl, vl, 0.4, True)
+    assert np.abs(o1[:, :, 0] - on[:, :, -1]).max() < 1e-15
+    # query i reads exactly keys 0 .. i + Nk - Nq: the same row of a square
+    # problem over the last Nq + shift positions
+    shift = 40 - 9
+    for i in (0, 4, 8):
+        oi, li = oracle.fwd(np.concatenate([np.zeros((2, 2, shift, 8)), q], axis=2),
+                            kl, vl, 0.4, True)
+        assert np.abs(oi[:, :, shift + i] - oc[:, :, i]).max() < 1e-14
+    rows = np.array([0, 5, 8, 3]); bh = np.array([0, 3, 1, 2])
+    orow, lrow = oracle.fwd_qk_rows(q, kl, vl, 0.4, True, bh, rows)
+    for t in range(4):
+        b, h = divmod(int(bh[t]), 2)
+        assert np.array_equal(orow[t], oc[b, h, rows[t]]) and lrow[t] == lc[b, h, rows[t]]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_unequal_lengths_mpmath(causal):
+    Nq, Nk, D = 3, 6, 3
+    q, k, v = _rand((1, 1, Nq, D), 35), _rand((1, 1, Nk, D), 36), _rand((1, 1, Nk, D), 37)
+    scale = 0.7
+    o, lse = oracle.fwd_qk(q, k, v, scale, causal)
+    mpmath.mp.dps = 50
+    for i in range(Nq):
+        n = i + Nk - Nq + 1 if causal else Nk
+        s = [mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(q[0, 0, i, d]) * mpmath.mpf(k[0, 0, j, d])
+                                             for d in range(D)) for j in range(n)]
+        w = [mpmath.e ** x for x in s]
+        tot = mpmath.fsum(w)
+        for d in range(D):
+            ref = mpmath.fsum(w[j] * mpmath.mpf(v[0, 0, j, d]) for j in range(n)) / tot
+            assert abs(o[0, 0, i, d] - float(ref)) <= 1e-13 * (1 + abs(float(ref)))
+        assert abs(lse[0, 0, i] - float(mpmath.log(tot))) < 1e-13
+
+
+def test_key_split_partials_merge_by_lse():
+    """Attention over disjoint key ranges combines exactly: L = logsumexp of
+    the partial L's and O = sum_s exp(L_s - L) O_s (the running-softmax rule of
+    tensortonic section 5 applied to whole ranges; the decode path splits the
+    keys this way)."""
+    q, k, v = _rand((2, 3, 4, 16), 38), _rand((2, 3, 300, 16), 39), _rand((2, 3, 300, 16), 40)
+    o, lse = oracle.fwd_qk(q, k, v, 0.25, False)
+    cuts = [0, 7, 130, 131, 300]
+    parts = [oracle.fwd_qk(q, k[:, :, a:b], v[:, :, a:b], 0.25, False)
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    L = scipy.special.logsumexp(np.stack([p[1] for p in parts]), axis=0)
+    O = sum(np.exp(p[1] - L)[..., None] * p[0] for p in parts)
+    assert np.abs(L - lse).max() < 1e-13 and np.abs(O - o).max() < 1e-13
