@@ -49,6 +49,8 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     lib.fa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]
     lib.fa_fwd.restype = _i
+    lib.fa_fwd_qk.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]
+    lib.fa_fwd_qk.restype = _i
     lib.fa_fwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                                   _i, _f, _i, _vp]
     lib.fa_fwd_varlen.restype = _i
@@ -129,6 +131,36 @@ def fa_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None,
                        _scale(softmax_scale, D), int(bool(causal)), _stream(stream))
     if rc != 0:
         raise FaError(rc, "fa_fwd")
+    return o, lse
+
+
+def fa_fwd_qk(q, k, v, softmax_scale=None, causal=False, out=None, lse=None,
+              return_lse=True, stream=None):
+    """Forward pass with Nq queries against Nk keys.  q: bf16 [B, H, Nq, D];
+    k, v: bf16 [B, H, Nk, D].  Under ``causal`` query i reads keys
+    j <= i + Nk - Nq (the queries are the last Nq positions).
+
+    Returns (o [B, H, Nq, D] bf16, lse [B, H, Nq] fp32 or None).
+    """
+    torch = _torch()
+    _check(q, "q")
+    B, H, Nq, D = q.shape
+    if k.dim() != 4:
+        raise ValueError("k must be [B, H, Nk, D]")
+    Nk = k.shape[2]
+    _check(k, "k", (B, H, Nk, D))
+    _check(v, "v", (B, H, Nk, D))
+    o = torch.empty_like(q) if out is None else out
+    _check(o, "out", q.shape)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq)
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32 [B, H, Nq]")
+    rc = load().fa_fwd_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk,
+                          D, _scale(softmax_scale, D), int(bool(causal)), _stream(stream))
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_qk")
     return o, lse
 
 

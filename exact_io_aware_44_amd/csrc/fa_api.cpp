@@ -76,7 +76,18 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            hipStream_t stream) {
     if (int rc = validate_fwd(q, k, v, o, lse, B, H, N, D, softmax_scale, causal))
         return rc;
-    fa::FwdArgs a{q, k, v, o, lse, nullptr, B, H, N, N, D, softmax_scale, causal != 0};
+    fa::FwdArgs a{q, k, v, o, lse, nullptr, B, H, N, N, D, softmax_scale, causal != 0, N};
+    return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int Nq, int Nk, int D, float softmax_scale, int causal,
+              hipStream_t stream) {
+    if (int rc = validate_fwd(q, k, v, o, lse, B, H, Nq, D, softmax_scale, causal))
+        return rc;
+    if (Nk < 1) return FA_ERR_SHAPE;
+    if (int rc = check_slice(Nk, D)) return rc;
+    fa::FwdArgs a{q, k, v, o, lse, nullptr, B, H, Nq, Nq, D, softmax_scale, causal != 0, Nk};
     return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -94,7 +105,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
     if (int rc = check_slice(total, D)) return rc;
     if (max_seqlen > total) max_seqlen = total;  // no sequence is longer than total
     fa::FwdArgs a{q, k, v, o, lse, cu_seqlens, nseq, H, total, max_seqlen, D,
-                  softmax_scale, causal != 0};
+                  softmax_scale, causal != 0, total};
     return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

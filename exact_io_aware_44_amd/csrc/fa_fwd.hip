@@ -96,7 +96,8 @@ struct FwdParams {
     float* lse;
     const int32_t* cu;
     int H;
-    int N;         // tokens per sequence (dense) or packed total (varlen)
+    int N;         // queries per sequence (dense) or packed total (varlen)
+    int Nk;        // keys per sequence (dense; varlen sequences use their own)
     int per_head;  // units per (batch, head): query tiles, or pairs if causal
     float c;       // softmax_scale * log2(e)
 };
@@ -133,18 +134,23 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     unit_of(blockIdx.x, gridDim.x, p.per_head, head, uidx);
     const int b = head / p.H, h = head - b * p.H;
 
-    int n;
-    int64_t row0;
+    // n queries attend to nk keys; under the causal mask query i reads keys
+    // j <= i + shift (shift = nk - n: the queries are the last n positions)
+    int n, nk;
+    int64_t row0, krow0;
     if constexpr (VARLEN) {
         int s = p.cu[b], e = p.cu[b + 1];
         s = min(max(s, 0), p.N);
         e = min(max(e, s), p.N);
-        n = e - s;
-        row0 = (int64_t)h * p.N + s;
+        n = nk = e - s;
+        row0 = krow0 = (int64_t)h * p.N + s;
     } else {
         n = p.N;
+        nk = p.Nk;
         row0 = ((int64_t)b * p.H + h) * p.N;
+        krow0 = ((int64_t)b * p.H + h) * p.Nk;
     }
+    const int shift = nk - n;
     // the query tiles of this unit, heavy first; ntiles is workgroup-uniform
     const int n_tiles = (n + T::BR - 1) / T::BR;
     int tile0 = uidx, tile1 = -1;
@@ -159,9 +165,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     const int ntiles = tile1 >= 0 ? 2 : 1;
 
     const uint32_t bytes = (uint32_t)n * D * 2;
+    const uint32_t kbytes = (uint32_t)nk * D * 2;
     const Buf qb = make_buf(p.q + row0 * D, bytes);
-    const Buf kb = make_buf(p.k + row0 * D, bytes);
-    const Buf vb = make_buf(p.v + row0 * D, bytes);
+    const Buf kb = make_buf(p.k + krow0 * D, kbytes);
+    const Buf vb = make_buf(p.v + krow0 * D, kbytes);
     const Buf ob = make_buf(p.o + row0 * D, bytes);
     const Buf lb = p.lse ? make_buf(p.lse + row0, (uint32_t)n * 4)
                          : make_buf(nullptr, 0);
@@ -208,7 +215,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         qreg[s] = __builtin_bit_cast(
             bf16x8, load16(qb, ((uint32_t)qi * D + 16 * s + 8 * hi) * 2));
 
-    const int kend = CAUSAL ? min(n, q0 + T::BR) : n;
+    // keys the tile reads: up to its last row's limit (none at all when
+    // every row precedes the first key)
+    const int kend = CAUSAL ? max(0, min(nk, q0 + T::BR + shift)) : nk;
     const int nkt = (kend + T::BC - 1) / T::BC;
 
     f32x16 acc[T::DB];
@@ -225,11 +234,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     // element mask: only on halves crossing the diagonal or the sequence end;
     // element r is allowed while its key offset stays below this lane's limit
     auto needs_mask = [&](int h) {
-        return (CAUSAL && 32 * h + 31 > q0) || 32 * h + 32 > n;
+        return (CAUSAL && 32 * h + 31 > q0 + shift) || 32 * h + 32 > nk;
     };
     auto apply_mask = [&](f32x16& s, int h) {
-        int lim = n - 32 * h;                              // keys before the end
-        if (CAUSAL) lim = min(lim, qi - 32 * h + 1);       // keys j <= qi
+        int lim = nk - 32 * h;                                  // keys before the end
+        if (CAUSAL) lim = min(lim, qi + shift - 32 * h + 1);    // keys j <= qi + shift
         lim -= 4 * hi;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -333,63 +342,67 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         }
     };
 
-    // ---- prologue: K_0, K_1, V_0 -> LDS; S of half 0; half-step 0 (S of
-    //      half 1 with the softmax of half 0) -------------------------------
-    load_k(0, k_lds0);
-    if (nkt > 1) load_k(T::BC, k_lds1);
-    load_v(0, v_lds0);
-    wait_vmem();  // Q registers and the first tiles landed
-    barrier_only();
-    f32x16 sA, sB;  // scores of even / odd halves
-    bf16x8 pA[2], pB[2];  // weights of even / odd halves
-    float alpha;
-    bool upd;
-    sA = f32x16{};
-#pragma unroll
-    for (int ss = 0; ss < T::DS; ++ss) sA = mfma32(k_op(k_lds0, 0, ss), qreg[ss], sA);
-    if (needs_mask(0)) apply_mask(sA, 0);
-    half_step(True{}, False{}, True{}, k_lds0, 1, nullptr, 0, sA, sB, pB, pA, alpha, upd);
-    l_run = l_new;  // first half: nothing to rescale
-    __syncthreads();  // K_0 is consumed before tile-step 0 reloads its buffer
-
-    // ---- tile-steps.  Tile-step j runs half-steps 2j+1 (odd: softmax sB ->
-    //      pB, S of half 2j+2 -> sA, P.V of half 2j with pA) and 2j+2 (even:
-    //      softmax sA -> pA, S of half 2j+3 -> sB, P.V of half 2j+1 with pB).
-    //      It reads only K tile j+1 (buffer (j+1)%2) and V tile j (buffer
-    //      j%2), so K_{j+2} and V_{j+1} load into the other buffers during
-    //      it; one barrier ends it. ---------------------------------------
-    // The buffer pointers are __restrict__: the tile a DMA is filling never
-    // overlaps a tile being read, which lets the compiler leave the loads in
-    // flight while the reads proceed.
-    auto tile_step = [&](int j, const bf16* __restrict__ k_rd, const bf16* __restrict__ v_rd,
-                         bf16* __restrict__ k_wr, bf16* __restrict__ v_wr) {
-        if (j + 2 < nkt) load_k((j + 2) * T::BC, k_wr);
-        load_v((j + 1) * T::BC, v_wr);
-        if (needs_mask(2 * j + 1)) apply_mask(sB, 2 * j + 1);
-        half_step(True{}, True{}, True{}, k_rd, 0, v_rd, 0, sB, sA, pA, pB, alpha, upd);
-        rescale(alpha, upd);
-        if (needs_mask(2 * j + 2)) apply_mask(sA, 2 * j + 2);
-        half_step(True{}, True{}, True{}, k_rd, 1, v_rd, 1, sA, sB, pB, pA, alpha, upd);
-        rescale(alpha, upd);
-        wait_vmem();  // K_{j+2} and V_{j+1} landed
+    // a tile whose queries all precede the first key reads nothing: O = 0,
+    // L = -inf (the epilogue below with zero sums)
+    if (nkt > 0) {
+        // ---- prologue: K_0, K_1, V_0 -> LDS; S of half 0; half-step 0 (S of
+        //      half 1 with the softmax of half 0) -------------------------------
+        load_k(0, k_lds0);
+        if (nkt > 1) load_k(T::BC, k_lds1);
+        load_v(0, v_lds0);
+        wait_vmem();  // Q registers and the first tiles landed
         barrier_only();
-    };
-    for (int j = 0; j + 1 < nkt; ++j) {
-        const bool odd = j & 1;
-        tile_step(j, odd ? k_lds0 : k_lds1, odd ? v_lds1 : v_lds0, odd ? k_lds1 : k_lds0,
-                  odd ? v_lds0 : v_lds1);
+        f32x16 sA, sB;  // scores of even / odd halves
+        bf16x8 pA[2], pB[2];  // weights of even / odd halves
+        float alpha;
+        bool upd;
+        sA = f32x16{};
+    #pragma unroll
+        for (int ss = 0; ss < T::DS; ++ss) sA = mfma32(k_op(k_lds0, 0, ss), qreg[ss], sA);
+        if (needs_mask(0)) apply_mask(sA, 0);
+        half_step(True{}, False{}, True{}, k_lds0, 1, nullptr, 0, sA, sB, pB, pA, alpha, upd);
+        l_run = l_new;  // first half: nothing to rescale
+        __syncthreads();  // K_0 is consumed before tile-step 0 reloads its buffer
+
+        // ---- tile-steps.  Tile-step j runs half-steps 2j+1 (odd: softmax sB ->
+        //      pB, S of half 2j+2 -> sA, P.V of half 2j with pA) and 2j+2 (even:
+        //      softmax sA -> pA, S of half 2j+3 -> sB, P.V of half 2j+1 with pB).
+        //      It reads only K tile j+1 (buffer (j+1)%2) and V tile j (buffer
+        //      j%2), so K_{j+2} and V_{j+1} load into the other buffers during
+        //      it; one barrier ends it. ---------------------------------------
+        // The buffer pointers are __restrict__: the tile a DMA is filling never
+        // overlaps a tile being read, which lets the compiler leave the loads in
+        // flight while the reads proceed.
+        auto tile_step = [&](int j, const bf16* __restrict__ k_rd, const bf16* __restrict__ v_rd,
+                             bf16* __restrict__ k_wr, bf16* __restrict__ v_wr) {
+            if (j + 2 < nkt) load_k((j + 2) * T::BC, k_wr);
+            load_v((j + 1) * T::BC, v_wr);
+            if (needs_mask(2 * j + 1)) apply_mask(sB, 2 * j + 1);
+            half_step(True{}, True{}, True{}, k_rd, 0, v_rd, 0, sB, sA, pA, pB, alpha, upd);
+            rescale(alpha, upd);
+            if (needs_mask(2 * j + 2)) apply_mask(sA, 2 * j + 2);
+            half_step(True{}, True{}, True{}, k_rd, 1, v_rd, 1, sA, sB, pB, pA, alpha, upd);
+            rescale(alpha, upd);
+            wait_vmem();  // K_{j+2} and V_{j+1} landed
+            barrier_only();
+        };
+        for (int j = 0; j + 1 < nkt; ++j) {
+            const bool odd = j & 1;
+            tile_step(j, odd ? k_lds0 : k_lds1, odd ? v_lds1 : v_lds0, odd ? k_lds1 : k_lds0,
+                      odd ? v_lds0 : v_lds1);
+        }
+        // last tile-step j = nkt - 1: softmax of half 2nkt-1 with P.V of half
+        // 2nkt-2, then P.V of half 2nkt-1
+        {
+            const int j = nkt - 1;
+            const bf16* v_rd = (j & 1) ? v_lds1 : v_lds0;
+            if (needs_mask(2 * j + 1)) apply_mask(sB, 2 * j + 1);
+            half_step(False{}, True{}, True{}, nullptr, 0, v_rd, 0, sB, sA, pA, pB, alpha, upd);
+            rescale(alpha, upd);
+            half_step(False{}, True{}, False{}, nullptr, 0, v_rd, 1, sA, sB, pB, pA, alpha, upd);
+        }
+        __syncthreads();  // LDS reads done before the next tile of the unit reloads
     }
-    // last tile-step j = nkt - 1: softmax of half 2nkt-1 with P.V of half
-    // 2nkt-2, then P.V of half 2nkt-1
-    {
-        const int j = nkt - 1;
-        const bf16* v_rd = (j & 1) ? v_lds1 : v_lds0;
-        if (needs_mask(2 * j + 1)) apply_mask(sB, 2 * j + 1);
-        half_step(False{}, True{}, True{}, nullptr, 0, v_rd, 0, sB, sA, pA, pB, alpha, upd);
-        rescale(alpha, upd);
-        half_step(False{}, True{}, False{}, nullptr, 0, v_rd, 1, sA, sB, pB, pA, alpha, upd);
-    }
-    __syncthreads();  // LDS reads done before the next tile of the unit reloads
 
     // epilogue: O = u / l (bf16), L = m + ln l (natural log, scaled units)
     const float l_tot = pair_sum(l_run);
@@ -422,6 +435,7 @@ hipError_t run_fwd(const FwdArgs& a, hipStream_t stream) {
     p.cu = a.cu;
     p.H = a.H;
     p.N = a.N;
+    p.Nk = a.Nk;
     const int n_qt = (a.max_seqlen + T::BR - 1) / T::BR;
     p.per_head = CAUSAL ? (n_qt + 1) / 2 : n_qt;
     p.c = (float)((double)a.scale * 1.4426950408889634);

@@ -17,11 +17,12 @@ struct FwdArgs {
     const int32_t* cu;      // packed offsets (varlen) or null (dense)
     int B;                  // batch (dense) or number of sequences (varlen)
     int H;
-    int N;                  // tokens per sequence (dense) or packed total
+    int N;                  // queries per sequence (dense) or packed total
     int max_seqlen;         // longest sequence (== N when dense)
     int D;
     float scale;
     bool causal;
+    int Nk;                 // keys per sequence (dense; == N when square)
 };
 
 struct BwdArgs {

@@ -89,6 +89,27 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            hipStream_t stream);
 
 /*
+ * Forward pass with Nq queries against Nk keys (chunked prefill, or queries
+ * against a longer key/value sequence).  tensortonic section 9 notes that
+ * the square causal mask is not right for every unequal-length layout; here
+ * the queries are the LAST Nq positions of the Nk-long sequence, so under the
+ * causal mask query i reads keys j <= i + Nk - Nq (the mask aligned
+ * bottom-right; Nq = Nk is the square mask of fa_fwd).  When Nq > Nk the
+ * first Nq - Nk queries read no key: their O rows are 0 and L is -inf.
+ *
+ *   q         in   bf16 [B, H, Nq, D]
+ *   k, v      in   bf16 [B, H, Nk, D]
+ *   o         out  bf16 [B, H, Nq, D]  (fully overwritten)
+ *   lse       out  fp32 [B, H, Nq]     (may be NULL)
+ *   B, H, Nq, Nk >= 1;  D in {64, 128};  causal in {0, 1}
+ *
+ * Same schedule, conventions and status codes as fa_fwd.
+ */
+int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int Nq, int Nk, int D, float softmax_scale, int causal,
+              hipStream_t stream);
+
+/*
  * Forward pass over packed variable-length sequences (nexusofnerds
  * "FlashAttention": variable-length packing; padding would otherwise waste
  * work).  nseq sequences are concatenated along the token axis; sequence b

@@ -35,7 +35,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert names == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd",
+    assert names == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_qk",
                      "fa_fwd_varlen", "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
@@ -71,6 +71,22 @@ def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=16, D=64, scale=0.125,
 ])
 def test_fwd_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code
+
+
+def fwd_qk(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=16, Nk=40, D=64, scale=0.125,
+           causal=1):
+    return lib.fa_fwd_qk(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(o=None), NULL),
+    (dict(B=0), SHAPE), (dict(Nq=0), SHAPE), (dict(Nk=0), SHAPE), (dict(Nk=-3), SHAPE),
+    (dict(H=70000), SHAPE), (dict(D=80), UNSUP), (dict(causal=3), UNSUP),
+    (dict(scale=float("nan")), ARG), (dict(v=PM), ALIGN), (dict(lse=P + 8), ALIGN),
+    (dict(Nk=1 << 23, D=128), TOO_LARGE), (dict(Nq=1 << 24, D=64), TOO_LARGE),
+])
+def test_fwd_qk_rejects(lib, kw, code):
+    assert fwd_qk(lib, **kw) == code
 
 
 def varlen(lib, q=P, k=P, v=P, o=P, lse=P, cu=P, nseq=2, total=32, maxlen=16,
