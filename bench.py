@@ -5,8 +5,9 @@ One step = one causal forward pass (fa_fwd) over the workload B4 H32 N4096
 D128 bf16 (iid N(0,1) inputs, scale 1/sqrt(128)), inputs resident in HBM.
 Prints ONE JSON line with the throughput in TFLOP/s, the roofline position of
 the forward kernel, the backward pass (fa_bwd, B2 H32 N4096 D128 causal)
-against the same roofline, and the fp64 CPU oracle timed on a bounded sample
-of the same workload.
+against the same roofline, the decoding-shaped forward (fa_fwd_splitkv, one
+query against a 16384-token cache, B8 H32 D128) against HBM bandwidth, and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
 
 FLOP convention: 4*D flops per (query, key) pair, causal counted as half of
 B*H*N^2 pairs; backward counted as 2.5x forward; softmax work not counted.
@@ -29,6 +30,7 @@ if ROOT not in sys.path:
 METRIC = "attention fwd TFLOP/s & % bf16 MFMA peak, causal B4 H32 N4096 D128"
 # MI355X dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 flop/clk/CU
 PEAK_BF16_TFLOPS = 2516.6
+HBM_GBS = 8000.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_causal_b4h32n4096d128_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_io_aware_44_amd", "csrc", f)
                   for f in ("fa_fwd.hip", "fa_device.hpp")]
@@ -140,12 +142,41 @@ def run_backward(torch, ai, fa, steps):
     return backward
 
 
+def run_decode(torch, ai, fa, steps):
+    """fa_fwd_splitkv on one new query per sequence against a 16384-token
+    cache (B8 H32 D128): HBM-bound, so reported as bytes per second."""
+    B, H, Nq, Nk, D = 8, 32, 1, 16384, 128
+    log("decode B%d H%d Nq%d Nk%d D%d" % (B, H, Nq, Nk, D))
+    q = ai.randn_bf16((B, H, Nq, D), 900).cuda()
+    k = ai.randn_bf16((B, H, Nk, D), 901).cuda()
+    v = ai.randn_bf16((B, H, Nk, D), 902).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, fa.fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D)),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        fa.fa_fwd_splitkv(q, k, v, causal=True, out=o, lse=lse, workspace=ws)
+
+    total, _ = time_launches(torch, step, steps, 5)
+    ms = total / steps
+    # algorithmic bytes: K and V read once, Q read and O, L written once
+    nbytes = 2 * B * H * Nk * D * 2 + 2 * B * H * Nq * D * 2 + B * H * Nq * 4
+    return {"workload": "decode B%d H%d Nq%d Nk%d D%d (split key ranges, LSE merge)"
+                        % (B, H, Nq, Nk, D),
+            "ms": round(ms, 4), "bound": "hbm", "unit": "GB/s",
+            "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": HBM_GBS,
+            "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_GBS, 4),
+            "bytes_per_call": nbytes, "launches": 2}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--bwd-steps", type=int, default=10)
+    ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -199,8 +230,9 @@ def main(argv=None):
     backward = None
     if args.bwd_steps > 0:
         backward = run_backward(torch, ai, fa, args.bwd_steps)
-
-
+    decode = None
+    if args.decode_steps > 0:
+        decode = run_decode(torch, ai, fa, args.decode_steps)
 
     line = {
         "metric": METRIC,
@@ -227,6 +259,7 @@ def main(argv=None):
                      "kernel": "fwd_kernel<128, causal>",
                      "avg_launch_ms": round(launch_ms, 5)},
         "backward": backward,
+        "decode": decode,
     }
     if rank == 0 and args.cpu_budget > 0:
         log("cpu baseline (oracle), about %.0f s" % args.cpu_budget)

@@ -51,6 +51,11 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd.restype = _i
     lib.fa_fwd_qk.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]
     lib.fa_fwd_qk.restype = _i
+    lib.fa_fwd_splitkv_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i]
+    lib.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
+    lib.fa_fwd_splitkv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i, _i,
+                                   _i, _i, _i, _f, _i, _i, _vp]
+    lib.fa_fwd_splitkv.restype = _i
     lib.fa_fwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                                   _i, _f, _i, _vp]
     lib.fa_fwd_varlen.restype = _i
@@ -161,6 +166,47 @@ def fa_fwd_qk(q, k, v, softmax_scale=None, causal=False, out=None, lse=None,
                           D, _scale(softmax_scale, D), int(bool(causal)), _stream(stream))
     if rc != 0:
         raise FaError(rc, "fa_fwd_qk")
+    return o, lse
+
+
+def fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, num_splits=0) -> int:
+    return int(load().fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, num_splits))
+
+
+def fa_fwd_splitkv(q, k, v, softmax_scale=None, causal=False, num_splits=0, out=None,
+                   lse=None, return_lse=True, workspace=None, stream=None):
+    """Decoding-shaped forward: q bf16 [B, H, Nq, D] against k, v bf16
+    [B, H, Nk, D], keys split across workgroups (``num_splits`` 0 = automatic)
+    and merged exactly.  Same result as fa_fwd_qk up to rounding.  A
+    workspace (uint8 GPU tensor) is allocated when not given.
+
+    Returns (o [B, H, Nq, D] bf16, lse [B, H, Nq] fp32 or None).
+    """
+    torch = _torch()
+    _check(q, "q")
+    B, H, Nq, D = q.shape
+    if k.dim() != 4:
+        raise ValueError("k must be [B, H, Nk, D]")
+    Nk = k.shape[2]
+    _check(k, "k", (B, H, Nk, D))
+    _check(v, "v", (B, H, Nk, D))
+    o = torch.empty_like(q) if out is None else out
+    _check(o, "out", q.shape)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq)
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32 [B, H, Nq]")
+    need = fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                               _ptr(workspace), ws_bytes, B, H, Nq, Nk, D,
+                               _scale(softmax_scale, D), int(bool(causal)), int(num_splits),
+                               _stream(stream))
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_splitkv")
     return o, lse
 
 

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -49,6 +50,33 @@ size_t workspace_bytes(int B, int H, int N) {
     return 2 * ((rows * sizeof(float) + 255) & ~(size_t)255);
 }
 
+// Key-range splits for fa_fwd_splitkv: the requested count (0 = automatic:
+// enough units for about 512 workgroups, two per CU, each range at least 256
+// keys; more ranges only add merge traffic and shorter streams),
+// clamped to one 64-key tile per range, then rounded so every range but the
+// last holds a whole number of tiles and none is empty.
+struct Splits {
+    int count;
+    int chunk;  // keys per range
+};
+Splits pick_splits(int B, int H, int Nq, int Nk, int requested) {
+    const int64_t units = (int64_t)B * H * ((Nq + 127) / 128);
+    int64_t s = requested;
+    if (s == 0) {
+        s = std::min<int64_t>(128, (512 + units - 1) / units);
+        s = std::min<int64_t>(s, std::max(1, (Nk + 255) / 256));
+    }
+    s = std::max<int64_t>(1, std::min<int64_t>(s, (Nk + 63) / 64));
+    const int chunk = (int)(((Nk + s - 1) / s + 63) / 64 * 64);
+    return Splits{(Nk + chunk - 1) / chunk, chunk};
+}
+// Partial O then partial L, fp32, each region padded to 256 bytes.
+size_t splitkv_bytes(int B, int H, int Nq, int D, int splits) {
+    if (splits <= 1) return 0;
+    const size_t rows = (size_t)B * H * Nq * splits;
+    return 4 * (((rows * D + 63) & ~(size_t)63) + ((rows + 63) & ~(size_t)63));
+}
+
 }  // namespace
 
 extern "C" {
@@ -62,9 +90,11 @@ const char* fa_status_string(int status) {
             return "FA_ERR_UNSUPPORTED: head width must be 64 or 128 and causal 0 or 1";
         case FA_ERR_ALIGN: return "FA_ERR_ALIGN: pointers must be 16-byte aligned";
         case FA_ERR_WORKSPACE:
-            return "FA_ERR_WORKSPACE: workspace is NULL or smaller than fa_bwd_workspace_size";
+            return "FA_ERR_WORKSPACE: workspace is NULL or smaller than the size its "
+                   "*_workspace_size function returns";
         case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: a kernel launch failed";
-        case FA_ERR_ARG: return "FA_ERR_ARG: softmax_scale must be finite and > 0";
+        case FA_ERR_ARG:
+            return "FA_ERR_ARG: softmax_scale must be finite and > 0, num_splits >= 0";
         case FA_ERR_TOO_LARGE:
             return "FA_ERR_TOO_LARGE: one (batch, head) slice exceeds 2 GiB";
         default: return "unknown fa status";
@@ -88,6 +118,34 @@ int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
     if (Nk < 1) return FA_ERR_SHAPE;
     if (int rc = check_slice(Nk, D)) return rc;
     fa::FwdArgs a{q, k, v, o, lse, nullptr, B, H, Nq, Nq, D, softmax_scale, causal != 0, Nk};
+    return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int D, int num_splits) {
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || num_splits < 0 || (D != 64 && D != 128))
+        return 0;
+    return splitkv_bytes(B, H, Nq, D, pick_splits(B, H, Nq, Nk, num_splits).count);
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, size_t ws_bytes, int B, int H, int Nq, int Nk, int D,
+                   float softmax_scale, int causal, int num_splits, hipStream_t stream) {
+    if (int rc = validate_fwd(q, k, v, o, lse, B, H, Nq, D, softmax_scale, causal))
+        return rc;
+    if (Nk < 1) return FA_ERR_SHAPE;
+    if (num_splits < 0) return FA_ERR_ARG;
+    if (int rc = check_slice(Nk, D)) return rc;
+    if (int rc = check_slice(2 * (int64_t)Nq, D)) return rc;  // fp32 partial rows
+    const Splits sp = pick_splits(B, H, Nq, Nk, num_splits);
+    fa::FwdArgs a{q, k, v, o, lse, nullptr, B, H, Nq, Nq, D, softmax_scale, causal != 0, Nk};
+    if (sp.count > 1) {
+        if (!workspace || ws_bytes < splitkv_bytes(B, H, Nq, D, sp.count))
+            return FA_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return FA_ERR_ALIGN;
+        a.splits = sp.count;
+        a.chunk = sp.chunk;
+        a.part = static_cast<float*>(workspace);
+    }
     return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -100,6 +100,14 @@ struct FwdParams {
     int Nk;        // keys per sequence (dense; varlen sequences use their own)
     int per_head;  // units per (batch, head): query tiles, or pairs if causal
     float c;       // softmax_scale * log2(e)
+    // split key ranges (decoding): unit (query tile, split s) reads keys
+    // [s * chunk, (s + 1) * chunk) and writes its normalised partial O (fp32)
+    // and L to part_o / part_l, row (s * B * H + head) * N + i
+    int splits;
+    int chunk;
+    int heads;     // B * H
+    float* part_o;
+    float* part_l;
 };
 
 // Unit schedule.  Workgroup i of a 1-D grid is dispatched to XCD i % 8; the
@@ -115,7 +123,7 @@ __device__ __forceinline__ void unit_of(int i, int total, int per_head, int& hea
 using True = std::true_type;
 using False = std::false_type;
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     using T = FwdTile<D>;
     // Separate LDS objects per buffer, always selected statically, so the
@@ -133,6 +141,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     int head, uidx;
     unit_of(blockIdx.x, gridDim.x, p.per_head, head, uidx);
     const int b = head / p.H, h = head - b * p.H;
+    int split = 0;
+    if constexpr (SPLIT) {
+        split = uidx % p.splits;
+        uidx /= p.splits;
+    }
 
     // n queries attend to nk keys; under the causal mask query i reads keys
     // j <= i + shift (shift = nk - n: the queries are the last n positions)
@@ -150,11 +163,19 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         row0 = ((int64_t)b * p.H + h) * p.N;
         krow0 = ((int64_t)b * p.H + h) * p.Nk;
     }
-    const int shift = nk - n;
+    int shift = nk - n;
+    // split mode: this unit reads keys [kbeg, kbeg + nk) of the sequence;
+    // rebasing K/V there keeps every key index below relative to the range
+    int kbeg = 0;
+    if constexpr (SPLIT) {
+        kbeg = min(nk, split * p.chunk);
+        nk = min(nk - kbeg, p.chunk);
+        shift -= kbeg;
+    }
     // the query tiles of this unit, heavy first; ntiles is workgroup-uniform
     const int n_tiles = (n + T::BR - 1) / T::BR;
     int tile0 = uidx, tile1 = -1;
-    if (CAUSAL) {
+    if (CAUSAL && !SPLIT) {
         tile0 = n_tiles - 1 - uidx;
         tile1 = uidx;
         if (tile1 > tile0) return;  // past the middle of this sequence's tiles
@@ -167,11 +188,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     const uint32_t bytes = (uint32_t)n * D * 2;
     const uint32_t kbytes = (uint32_t)nk * D * 2;
     const Buf qb = make_buf(p.q + row0 * D, bytes);
-    const Buf kb = make_buf(p.k + krow0 * D, kbytes);
-    const Buf vb = make_buf(p.v + krow0 * D, kbytes);
+    const Buf kb = make_buf(p.k + (krow0 + kbeg) * D, kbytes);
+    const Buf vb = make_buf(p.v + (krow0 + kbeg) * D, kbytes);
     const Buf ob = make_buf(p.o + row0 * D, bytes);
     const Buf lb = p.lse ? make_buf(p.lse + row0, (uint32_t)n * 4)
                          : make_buf(nullptr, 0);
+    // split mode: partial outputs of this key range (fp32)
+    const int64_t prow0 = ((int64_t)split * p.heads + head) * n;
+    const Buf pob = SPLIT ? make_buf(p.part_o + prow0 * D, (uint32_t)n * D * 4)
+                          : make_buf(nullptr, 0);
+    const Buf plb = SPLIT ? make_buf(p.part_l + prow0, (uint32_t)n * 4)
+                          : make_buf(nullptr, 0);
 
     // ---- tile movement: global -> LDS directly (no staging registers).
     //      Wave w issues the wave-wide 1 KiB loads w, w+4, ...; each lane's
@@ -404,26 +431,62 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         __syncthreads();  // LDS reads done before the next tile of the unit reloads
     }
 
-    // epilogue: O = u / l (bf16), L = m + ln l (natural log, scaled units)
+    // epilogue: O = u / l (bf16), L = m + ln l (natural log, scaled units);
+    // in split mode the same quantities of the key range, in fp32
     const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float L = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : kNegInf;
 #pragma unroll
     for (int e = 0; e < T::DB; ++e)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const int d = 32 * e + 8 * r4 + 4 * hi;
-            store8(ob, ((uint32_t)qi * D + d) * 2,
-                   pack4(acc[e][4 * r4] * inv, acc[e][4 * r4 + 1] * inv,
-                         acc[e][4 * r4 + 2] * inv, acc[e][4 * r4 + 3] * inv));
+            if constexpr (SPLIT) {
+                const f32x4 ov{acc[e][4 * r4] * inv, acc[e][4 * r4 + 1] * inv,
+                               acc[e][4 * r4 + 2] * inv, acc[e][4 * r4 + 3] * inv};
+                store16(pob, ((uint32_t)qi * D + d) * 4, __builtin_bit_cast(u32x4, ov));
+            } else {
+                store8(ob, ((uint32_t)qi * D + d) * 2,
+                       pack4(acc[e][4 * r4] * inv, acc[e][4 * r4 + 1] * inv,
+                             acc[e][4 * r4 + 2] * inv, acc[e][4 * r4 + 3] * inv));
+            }
         }
-    if (hi == 0) {
-        const float L = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : kNegInf;
-        store4(lb, (uint32_t)qi * 4, __builtin_bit_cast(uint32_t, L));
-    }
+    if (hi == 0) store4(SPLIT ? plb : lb, (uint32_t)qi * 4, __builtin_bit_cast(uint32_t, L));
     }  // query tiles of the unit
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+// Split key ranges, second step: per query row, L = ln sum_s exp(L_s) and
+// O = sum_s exp(L_s - L) O_s (the running-softmax rule of tensortonic
+// section 5 applied to whole key ranges).  One thread per 4 output columns.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(const float* part_o, const float* part_l,
+                                                    bf16* o, float* lse, int64_t rows,
+                                                    int splits) {
+    constexpr int TPR = D / 4;  // threads per row
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gid / TPR;
+    const int c = (int)(gid % TPR);
+    if (row >= rows) return;
+    float m = kNegInf;
+    for (int s = 0; s < splits; ++s) m = fmaxf(m, part_l[s * rows + row]);
+    f32x4 acc{0.f, 0.f, 0.f, 0.f};
+    float L = kNegInf;
+    if (m != kNegInf) {  // some range had a readable key
+        float sum = 0.f;
+        for (int s = 0; s < splits; ++s) sum += exp2_fast((part_l[s * rows + row] - m) * kLog2e);
+        const float inv = 1.f / sum;
+        for (int s = 0; s < splits; ++s) {
+            const float w = exp2_fast((part_l[s * rows + row] - m) * kLog2e) * inv;
+            const f32x4 po = *reinterpret_cast<const f32x4*>(part_o + (s * rows + row) * D + 4 * c);
+            acc += w * po;
+        }
+        L = m + log2_fast(sum) * kLn2;
+    }
+    *reinterpret_cast<u32x2*>(o + row * D + 4 * c) = pack4(acc[0], acc[1], acc[2], acc[3]);
+    if (lse && c == 0) lse[row] = L;
+}
+
+template <int D, bool CAUSAL, bool VARLEN, bool SPLIT>
 hipError_t run_fwd(const FwdArgs& a, hipStream_t stream) {
     using T = FwdTile<D>;
     FwdParams p;
@@ -437,22 +500,37 @@ hipError_t run_fwd(const FwdArgs& a, hipStream_t stream) {
     p.N = a.N;
     p.Nk = a.Nk;
     const int n_qt = (a.max_seqlen + T::BR - 1) / T::BR;
-    p.per_head = CAUSAL ? (n_qt + 1) / 2 : n_qt;
+    p.per_head = SPLIT ? n_qt * a.splits : CAUSAL ? (n_qt + 1) / 2 : n_qt;
     p.c = (float)((double)a.scale * 1.4426950408889634);
+    p.splits = a.splits;
+    p.chunk = a.chunk;
+    p.heads = a.B * a.H;
+    const int64_t rows = (int64_t)a.B * a.H * a.N;
+    p.part_o = a.part;
+    p.part_l = a.part + ((rows * a.splits * D + 63) & ~(int64_t)63);
     const int64_t units = (int64_t)p.per_head * a.H * a.B;
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)units),
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, VARLEN, SPLIT>), dim3((unsigned)units),
                        dim3(T::THREADS), 0, stream, p);
+    if (!SPLIT) return hipGetLastError();
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t threads = rows * (D / 4);
+    hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                       0, stream, p.part_o, p.part_l, p.o, p.lse, rows, a.splits);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t run_fwd_d(const FwdArgs& a, hipStream_t stream) {
     const bool varlen = a.cu != nullptr;
+    if (a.splits > 1)
+        return a.causal ? run_fwd<D, true, false, true>(a, stream)
+                        : run_fwd<D, false, false, true>(a, stream);
     if (a.causal)
-        return varlen ? run_fwd<D, true, true>(a, stream)
-                      : run_fwd<D, true, false>(a, stream);
-    return varlen ? run_fwd<D, false, true>(a, stream)
-                  : run_fwd<D, false, false>(a, stream);
+        return varlen ? run_fwd<D, true, true, false>(a, stream)
+                      : run_fwd<D, true, false, false>(a, stream);
+    return varlen ? run_fwd<D, false, true, false>(a, stream)
+                  : run_fwd<D, false, false, false>(a, stream);
 }
 
 }  // namespace

@@ -23,6 +23,9 @@ struct FwdArgs {
     float scale;
     bool causal;
     int Nk;                 // keys per sequence (dense; == N when square)
+    int splits = 1;         // > 1: key ranges split across units (dense only)
+    int chunk = 0;          // keys per split, a multiple of 64
+    float* part = nullptr;  // split workspace: partial O, then partial L (fp32)
 };
 
 struct BwdArgs {

@@ -61,7 +61,8 @@ enum fa_status {
     FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
     FA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required         */
     FA_ERR_LAUNCH = 6,      /* a kernel launch failed (HIP error)              */
-    FA_ERR_ARG = 7,         /* softmax_scale not finite or not > 0             */
+    FA_ERR_ARG = 7,         /* softmax_scale not finite or not > 0, or a
+                               negative num_splits                             */
     FA_ERR_TOO_LARGE = 8    /* a (batch, head) slice exceeds 2 GiB             */
 };
 
@@ -108,6 +109,40 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int Nq, int Nk, int D, float softmax_scale, int causal,
               hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_fwd_splitkv needs for these sizes and this
+ * num_splits (0 when it will not split, or when the sizes are invalid).
+ */
+size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int D, int num_splits);
+
+/*
+ * Decoding-shaped forward: few queries against a long key/value sequence
+ * (tensortonic section 8: a cached generation step has one new query and a
+ * long run of past keys and values, a different workload that needs kernels
+ * suited to its shape).  The keys of every (batch, head) are split into
+ * ranges handled by separate workgroups, so a handful of query rows still
+ * fill the GPU; each range yields its normalised partial O_s and L_s, and a
+ * second kernel combines them exactly: L = ln sum_s exp(L_s) and
+ * O = sum_s exp(L_s - L) O_s (the running-softmax rescale of section 5
+ * applied to whole ranges).  The result is that of fa_fwd_qk on the same
+ * arguments, up to rounding.
+ *
+ *   q, k, v, o, lse, B, H, Nq, Nk, D, causal   as for fa_fwd_qk
+ *   num_splits  0 = choose automatically (about 512 workgroups in total,
+ *               ranges of at least 256 keys); > 0 = that many ranges, at
+ *               most one per 64 keys.  With one range no workspace is used.
+ *   workspace   device memory of fa_fwd_splitkv_workspace_size(B, H, Nq, Nk,
+ *               D, num_splits) bytes (may be NULL when that is 0); contents
+ *               on entry ignored, on exit unspecified
+ *
+ * Returns FA_OK or an fa_status code (FA_ERR_WORKSPACE when the workspace is
+ * missing or short).
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk,
+                   int D, float softmax_scale, int causal, int num_splits,
+                   hipStream_t stream);
 
 /*
  * Forward pass over packed variable-length sequences (nexusofnerds

@@ -36,6 +36,7 @@ def _declared():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert names == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_qk",
+                     "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
                      "fa_fwd_varlen", "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
@@ -87,6 +88,36 @@ def fwd_qk(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=16, Nk=40, D=64, scale=0
 ])
 def test_fwd_qk_rejects(lib, kw, code):
     assert fwd_qk(lib, **kw) == code
+
+
+def splitkv(lib, q=P, k=P, v=P, o=P, lse=P, ws=P, ws_bytes=1 << 30, B=2, H=4, Nq=1,
+            Nk=4096, D=128, scale=0.1, causal=1, splits=0):
+    return lib.fa_fwd_splitkv(q, k, v, o, lse, ws, ws_bytes, B, H, Nq, Nk, D, scale,
+                              causal, splits, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(v=None), NULL), (dict(B=0), SHAPE), (dict(Nk=0), SHAPE),
+    (dict(Nq=-1), SHAPE), (dict(D=48), UNSUP), (dict(causal=7), UNSUP),
+    (dict(scale=0.0), ARG), (dict(splits=-2), ARG), (dict(o=PM), ALIGN),
+    (dict(ws=None), WS), (dict(ws_bytes=1000), WS), (dict(ws=PM), ALIGN),
+    (dict(Nk=1 << 23), TOO_LARGE), (dict(Nq=1 << 22), TOO_LARGE),
+])
+def test_splitkv_rejects(lib, kw, code):
+    assert splitkv(lib, **kw) == code
+
+
+def test_splitkv_workspace_size():
+    ws = fa.fa_fwd_splitkv_workspace_size
+    # B2 H4 Nq1 Nk4096: automatic count min(128, 512/8, 4096/256) = 16 ranges
+    # of 256 keys; partial O (16*8 rows * 128 fp32) then partial L (padded)
+    assert ws(2, 4, 1, 4096, 128) == 4 * (16 * 8 * 128 + 128)
+    assert ws(2, 4, 1, 4096, 128, 4) == 4 * (4 * 8 * 128 + 64)
+    assert ws(2, 4, 1, 4096, 128, 1) == 0       # one range: plain forward
+    assert ws(64, 32, 1, 200, 128) == 0         # enough heads and a short cache
+    assert ws(1, 1, 1, 100, 64, 50) == 4 * (2 * 64 + 64)  # at most one range per 64 keys
+    assert ws(0, 4, 1, 4096, 128) == 0 and ws(2, 4, 1, 4096, 96) == 0
+    assert ws(2, 4, 1, 4096, 128, -1) == 0
 
 
 def varlen(lib, q=P, k=P, v=P, o=P, lse=P, cu=P, nseq=2, total=32, maxlen=16,
