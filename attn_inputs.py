@@ -51,6 +51,13 @@ def randn_bf16(shape, seed: int | torch.Generator, chunk_rows: int = 0):
     return out
 
 
+def randn_f16(shape, seed: int | torch.Generator):
+    """iid N(0,1) fp32 from a seeded CPU generator, rounded to IEEE fp16."""
+    g = generator(seed) if isinstance(seed, int) else seed
+    return torch.randn(tuple(int(s) for s in shape), generator=g,
+                       dtype=torch.float32).to(torch.float16)
+
+
 def qkv(B: int, H: int, N: int, D: int, seed: int, chunk_rows: int = 0):
     """Q, K, V as bf16 [B, H, N, D], drawn in that order from one generator."""
     g = generator(seed)

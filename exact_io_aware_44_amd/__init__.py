@@ -5,7 +5,8 @@ function here only marshals arguments: it checks tensor dtype, device and
 shape, allocates outputs with torch when the caller passes none, and hands raw
 device pointers plus the current HIP stream to the library.  All arithmetic
 runs in the library's HIP kernels; there is no CPU or PyTorch fallback, and a
-missing library raises.
+missing library raises.  Tensors are bfloat16 or float16 (all 16-bit
+tensors of a call share q's type; float16 calls go to the *_f16 entry points).
 """
 from __future__ import annotations
 
@@ -13,7 +14,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["load", "build", "FaError", "fa_fwd", "fa_fwd_varlen", "fa_bwd",
+__all__ = ["load", "build", "FaError", "fa_fwd", "fa_fwd_qk", "fa_fwd_splitkv",
+           "fa_fwd_splitkv_workspace_size", "fa_fwd_varlen", "fa_bwd",
            "fa_bwd_workspace_size", "fa_status_string", "LIB_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +68,10 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd.restype = _i
     lib.fa_status_string.argtypes = [_i]
     lib.fa_status_string.restype = ctypes.c_char_p
+    for name in ("fa_fwd", "fa_fwd_qk", "fa_fwd_splitkv", "fa_fwd_varlen", "fa_bwd"):
+        f16 = getattr(lib, name + "_f16")  # the fp16 twin: same arguments
+        f16.argtypes = getattr(lib, name).argtypes
+        f16.restype = _i
     _lib = lib
     return lib
 
@@ -84,10 +90,14 @@ def _torch():
     return torch
 
 
-def _check(t, name, shape=None):
+def _check(t, name, shape=None, dtype=None):
+    """GPU, contiguous, 16-bit (bf16 or fp16; ``dtype`` when given: the
+    tensors of one call share q's element type), optionally of ``shape``."""
     torch = _torch()
-    if t.dtype != torch.bfloat16:
-        raise TypeError("%s must be bfloat16, got %s" % (name, t.dtype))
+    if dtype is None and t.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("%s must be bfloat16 or float16, got %s" % (name, t.dtype))
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s like q, got %s" % (name, dtype, t.dtype))
     if not t.is_cuda:
         raise ValueError("%s must be a GPU tensor" % name)
     if not t.is_contiguous():
@@ -95,6 +105,11 @@ def _check(t, name, shape=None):
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape),
                                                          tuple(shape)))
+
+
+def _fn(name, q):
+    """The entry point for q's element type (the _f16 twin for float16)."""
+    return getattr(load(), name + ("_f16" if q.dtype == _torch().float16 else ""))
 
 
 def _stream(stream):
@@ -123,16 +138,16 @@ def fa_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None,
     torch = _torch()
     _check(q, "q")
     B, H, N, D = q.shape
-    _check(k, "k", q.shape)
-    _check(v, "v", q.shape)
+    _check(k, "k", q.shape, q.dtype)
+    _check(v, "v", q.shape, q.dtype)
     o = torch.empty_like(q) if out is None else out
-    _check(o, "out", q.shape)
+    _check(o, "out", q.shape, q.dtype)
     if lse is None and return_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
                             or not lse.is_contiguous()):
         raise ValueError("lse must be contiguous float32 [B, H, N]")
-    rc = load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, D,
+    rc = _fn("fa_fwd", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, D,
                        _scale(softmax_scale, D), int(bool(causal)), _stream(stream))
     if rc != 0:
         raise FaError(rc, "fa_fwd")
@@ -153,16 +168,16 @@ def fa_fwd_qk(q, k, v, softmax_scale=None, causal=False, out=None, lse=None,
     if k.dim() != 4:
         raise ValueError("k must be [B, H, Nk, D]")
     Nk = k.shape[2]
-    _check(k, "k", (B, H, Nk, D))
-    _check(v, "v", (B, H, Nk, D))
+    _check(k, "k", (B, H, Nk, D), q.dtype)
+    _check(v, "v", (B, H, Nk, D), q.dtype)
     o = torch.empty_like(q) if out is None else out
-    _check(o, "out", q.shape)
+    _check(o, "out", q.shape, q.dtype)
     if lse is None and return_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq)
                             or not lse.is_contiguous()):
         raise ValueError("lse must be contiguous float32 [B, H, Nq]")
-    rc = load().fa_fwd_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk,
+    rc = _fn("fa_fwd_qk", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk,
                           D, _scale(softmax_scale, D), int(bool(causal)), _stream(stream))
     if rc != 0:
         raise FaError(rc, "fa_fwd_qk")
@@ -188,10 +203,10 @@ def fa_fwd_splitkv(q, k, v, softmax_scale=None, causal=False, num_splits=0, out=
     if k.dim() != 4:
         raise ValueError("k must be [B, H, Nk, D]")
     Nk = k.shape[2]
-    _check(k, "k", (B, H, Nk, D))
-    _check(v, "v", (B, H, Nk, D))
+    _check(k, "k", (B, H, Nk, D), q.dtype)
+    _check(v, "v", (B, H, Nk, D), q.dtype)
     o = torch.empty_like(q) if out is None else out
-    _check(o, "out", q.shape)
+    _check(o, "out", q.shape, q.dtype)
     if lse is None and return_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq)
@@ -201,7 +216,7 @@ def fa_fwd_splitkv(q, k, v, softmax_scale=None, causal=False, num_splits=0, out=
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = load().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+    rc = _fn("fa_fwd_splitkv", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                _ptr(workspace), ws_bytes, B, H, Nq, Nk, D,
                                _scale(softmax_scale, D), int(bool(causal)), int(num_splits),
                                _stream(stream))
@@ -220,16 +235,16 @@ def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None,
     torch = _torch()
     _check(q, "q")
     H, total, D = q.shape
-    _check(k, "k", q.shape)
-    _check(v, "v", q.shape)
+    _check(k, "k", q.shape, q.dtype)
+    _check(v, "v", q.shape, q.dtype)
     if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
         raise ValueError("cu_seqlens must be a 1-D int32 GPU tensor")
     nseq = cu_seqlens.shape[0] - 1
     o = torch.empty_like(q) if out is None else out
-    _check(o, "out", q.shape)
+    _check(o, "out", q.shape, q.dtype)
     if lse is None and return_lse:
         lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
-    rc = load().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+    rc = _fn("fa_fwd_varlen", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                               _ptr(cu_seqlens), nseq, total, int(max_seqlen), H, D,
                               _scale(softmax_scale, D), int(bool(causal)),
                               _stream(stream))
@@ -242,22 +257,24 @@ def fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None,
            dk=None, dv=None, workspace=None, stream=None):
     """Backward pass.  o and lse must come from fa_fwd on the same inputs.
 
-    Returns (dq, dk, dv), bf16 [B, H, N, D].  ``workspace`` (uint8 GPU tensor
+    Returns (dq, dk, dv) [B, H, N, D] in q's element type.  ``workspace`` (uint8 GPU tensor
     of at least fa_bwd_workspace_size bytes) is allocated when not given.
     """
     torch = _torch()
     for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
-        _check(t, name, q.shape)
+        _check(t, name, q.shape, q.dtype)
     B, H, N, D = q.shape
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous float32 [B, H, N]")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, name, q.shape, q.dtype)
     ws_bytes = fa_bwd_workspace_size(B, H, N, D)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-    rc = load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+    rc = _fn("fa_bwd", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                        workspace.numel() * workspace.element_size(), B, H, N, D,
                        _scale(softmax_scale, D), int(bool(causal)), _stream(stream))

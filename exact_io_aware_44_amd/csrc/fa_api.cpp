@@ -77,9 +77,98 @@ size_t splitkv_bytes(int B, int H, int Nq, int D, int splits) {
     return 4 * (((rows * D + 63) & ~(size_t)63) + ((rows + 63) & ~(size_t)63));
 }
 
+// ---- the entry points, parameterised by the element type (bf16 / fp16) ----
+
+int fwd_impl(bool f16, const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int N, int D, float softmax_scale, int causal,
+             hipStream_t stream) {
+    if (int rc = validate_fwd(q, k, v, o, lse, B, H, N, D, softmax_scale, causal))
+        return rc;
+    fa::FwdArgs a{q, k, v, o, lse, nullptr, B, H, N, N, D, softmax_scale, causal != 0, N};
+    a.f16 = f16;
+    return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fwd_qk_impl(bool f16, const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int Nq, int Nk, int D, float softmax_scale, int causal,
+                hipStream_t stream) {
+    if (int rc = validate_fwd(q, k, v, o, lse, B, H, Nq, D, softmax_scale, causal))
+        return rc;
+    if (Nk < 1) return FA_ERR_SHAPE;
+    if (int rc = check_slice(Nk, D)) return rc;
+    fa::FwdArgs a{q, k, v, o, lse, nullptr, B, H, Nq, Nq, D, softmax_scale, causal != 0, Nk};
+    a.f16 = f16;
+    return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fwd_splitkv_impl(bool f16, const void* q, const void* k, const void* v, void* o,
+                     float* lse, void* workspace, size_t ws_bytes, int B, int H, int Nq,
+                     int Nk, int D, float softmax_scale, int causal, int num_splits,
+                     hipStream_t stream) {
+    if (int rc = validate_fwd(q, k, v, o, lse, B, H, Nq, D, softmax_scale, causal))
+        return rc;
+    if (Nk < 1) return FA_ERR_SHAPE;
+    if (num_splits < 0) return FA_ERR_ARG;
+    if (int rc = check_slice(Nk, D)) return rc;
+    if (int rc = check_slice(2 * (int64_t)Nq, D)) return rc;  // fp32 partial rows
+    const Splits sp = pick_splits(B, H, Nq, Nk, num_splits);
+    fa::FwdArgs a{q, k, v, o, lse, nullptr, B, H, Nq, Nq, D, softmax_scale, causal != 0, Nk};
+    if (sp.count > 1) {
+        if (!workspace || ws_bytes < splitkv_bytes(B, H, Nq, D, sp.count))
+            return FA_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return FA_ERR_ALIGN;
+        a.splits = sp.count;
+        a.chunk = sp.chunk;
+        a.part = static_cast<float*>(workspace);
+    }
+    a.f16 = f16;
+    return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fwd_varlen_impl(bool f16, const void* q, const void* k, const void* v, void* o,
+                    float* lse, const int32_t* cu_seqlens, int nseq, int total,
+                    int max_seqlen, int H, int D, float softmax_scale, int causal,
+                    hipStream_t stream) {
+    if (!q || !k || !v || !o || !cu_seqlens) return FA_ERR_NULL;
+    if (nseq < 1 || total < 1 || max_seqlen < 1 || nseq > 65535) return FA_ERR_SHAPE;
+    if (int rc = check_common(H, D, softmax_scale, causal)) return rc;
+    if (H > 65535) return FA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        (lse && !aligned16(lse)) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+        return FA_ERR_ALIGN;
+    if (int rc = check_slice(total, D)) return rc;
+    if (max_seqlen > total) max_seqlen = total;  // no sequence is longer than total
+    fa::FwdArgs a{q, k, v, o, lse, cu_seqlens, nseq, H, total, max_seqlen, D,
+                  softmax_scale, causal != 0, total};
+    a.f16 = f16;
+    return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int bwd_impl(bool f16, const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+             void* workspace, size_t ws_bytes, int B, int H, int N, int D,
+             float softmax_scale, int causal, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+    if (B < 1 || N < 1) return FA_ERR_SHAPE;
+    if (int rc = check_common(H, D, softmax_scale, causal)) return rc;
+    if (B > 65535 || H > 65535) return FA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+        !aligned16(dv))
+        return FA_ERR_ALIGN;
+    if (int rc = check_slice(N, D)) return rc;
+    if (!workspace || ws_bytes < workspace_bytes(B, H, N)) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace),
+                  B, H, N, D, softmax_scale, causal != 0};
+    a.f16 = f16;
+    return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
+
 
 const char* fa_status_string(int status) {
     switch (status) {
@@ -101,70 +190,10 @@ const char* fa_status_string(int status) {
     }
 }
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-           int B, int H, int N, int D, float softmax_scale, int causal,
-           hipStream_t stream) {
-    if (int rc = validate_fwd(q, k, v, o, lse, B, H, N, D, softmax_scale, causal))
-        return rc;
-    fa::FwdArgs a{q, k, v, o, lse, nullptr, B, H, N, N, D, softmax_scale, causal != 0, N};
-    return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
-}
-
-int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
-              int B, int H, int Nq, int Nk, int D, float softmax_scale, int causal,
-              hipStream_t stream) {
-    if (int rc = validate_fwd(q, k, v, o, lse, B, H, Nq, D, softmax_scale, causal))
-        return rc;
-    if (Nk < 1) return FA_ERR_SHAPE;
-    if (int rc = check_slice(Nk, D)) return rc;
-    fa::FwdArgs a{q, k, v, o, lse, nullptr, B, H, Nq, Nq, D, softmax_scale, causal != 0, Nk};
-    return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
-}
-
 size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int D, int num_splits) {
     if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || num_splits < 0 || (D != 64 && D != 128))
         return 0;
     return splitkv_bytes(B, H, Nq, D, pick_splits(B, H, Nq, Nk, num_splits).count);
-}
-
-int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
-                   void* workspace, size_t ws_bytes, int B, int H, int Nq, int Nk, int D,
-                   float softmax_scale, int causal, int num_splits, hipStream_t stream) {
-    if (int rc = validate_fwd(q, k, v, o, lse, B, H, Nq, D, softmax_scale, causal))
-        return rc;
-    if (Nk < 1) return FA_ERR_SHAPE;
-    if (num_splits < 0) return FA_ERR_ARG;
-    if (int rc = check_slice(Nk, D)) return rc;
-    if (int rc = check_slice(2 * (int64_t)Nq, D)) return rc;  // fp32 partial rows
-    const Splits sp = pick_splits(B, H, Nq, Nk, num_splits);
-    fa::FwdArgs a{q, k, v, o, lse, nullptr, B, H, Nq, Nq, D, softmax_scale, causal != 0, Nk};
-    if (sp.count > 1) {
-        if (!workspace || ws_bytes < splitkv_bytes(B, H, Nq, D, sp.count))
-            return FA_ERR_WORKSPACE;
-        if (!aligned16(workspace)) return FA_ERR_ALIGN;
-        a.splits = sp.count;
-        a.chunk = sp.chunk;
-        a.part = static_cast<float*>(workspace);
-    }
-    return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
-}
-
-int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
-                  float* lse, const int32_t* cu_seqlens, int nseq, int total,
-                  int max_seqlen, int H, int D, float softmax_scale, int causal,
-                  hipStream_t stream) {
-    if (!q || !k || !v || !o || !cu_seqlens) return FA_ERR_NULL;
-    if (nseq < 1 || total < 1 || max_seqlen < 1 || nseq > 65535) return FA_ERR_SHAPE;
-    if (int rc = check_common(H, D, softmax_scale, causal)) return rc;
-    if (H > 65535) return FA_ERR_SHAPE;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-        (lse && !aligned16(lse)) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
-        return FA_ERR_ALIGN;
-    if (int rc = check_slice(total, D)) return rc;
-    if (max_seqlen > total) max_seqlen = total;  // no sequence is longer than total
-    fa::FwdArgs a{q, k, v, o, lse, cu_seqlens, nseq, H, total, max_seqlen, D,
-                  softmax_scale, causal != 0, total};
-    return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int D) {
@@ -172,24 +201,67 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int D) {
     return workspace_bytes(B, H, N);
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o,
-           const float* lse, const void* dout, void* dq, void* dk, void* dv,
-           void* workspace, size_t ws_bytes, int B, int H, int N, int D,
-           float softmax_scale, int causal, hipStream_t stream) {
-    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
-    if (B < 1 || N < 1) return FA_ERR_SHAPE;
-    if (int rc = check_common(H, D, softmax_scale, causal)) return rc;
-    if (B > 65535 || H > 65535) return FA_ERR_SHAPE;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-        !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
-        !aligned16(dv))
-        return FA_ERR_ALIGN;
-    if (int rc = check_slice(N, D)) return rc;
-    if (!workspace || ws_bytes < workspace_bytes(B, H, N)) return FA_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return FA_ERR_ALIGN;
-    fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace),
-                  B, H, N, D, softmax_scale, causal != 0};
-    return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+           int N, int D, float softmax_scale, int causal, hipStream_t stream) {
+    return fwd_impl(false, q, k, v, o, lse, B, H, N, D, softmax_scale, causal, stream);
+}
+int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+               int H, int N, int D, float softmax_scale, int causal, hipStream_t stream) {
+    return fwd_impl(true, q, k, v, o, lse, B, H, N, D, softmax_scale, causal, stream);
+}
+
+int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int Nq, int Nk, int D, float softmax_scale, int causal, hipStream_t stream) {
+    return fwd_qk_impl(false, q, k, v, o, lse, B, H, Nq, Nk, D, softmax_scale, causal,
+                       stream);
+}
+int fa_fwd_qk_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                  int H, int Nq, int Nk, int D, float softmax_scale, int causal,
+                  hipStream_t stream) {
+    return fwd_qk_impl(true, q, k, v, o, lse, B, H, Nq, Nk, D, softmax_scale, causal,
+                       stream);
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, size_t ws_bytes, int B, int H, int Nq, int Nk, int D,
+                   float softmax_scale, int causal, int num_splits, hipStream_t stream) {
+    return fwd_splitkv_impl(false, q, k, v, o, lse, workspace, ws_bytes, B, H, Nq, Nk, D,
+                            softmax_scale, causal, num_splits, stream);
+}
+int fa_fwd_splitkv_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                       void* workspace, size_t ws_bytes, int B, int H, int Nq, int Nk,
+                       int D, float softmax_scale, int causal, int num_splits,
+                       hipStream_t stream) {
+    return fwd_splitkv_impl(true, q, k, v, o, lse, workspace, ws_bytes, B, H, Nq, Nk, D,
+                            softmax_scale, causal, num_splits, stream);
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int32_t* cu_seqlens, int nseq, int total, int max_seqlen, int H,
+                  int D, float softmax_scale, int causal, hipStream_t stream) {
+    return fwd_varlen_impl(false, q, k, v, o, lse, cu_seqlens, nseq, total, max_seqlen, H,
+                           D, softmax_scale, causal, stream);
+}
+int fa_fwd_varlen_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int32_t* cu_seqlens, int nseq, int total, int max_seqlen, int H,
+                      int D, float softmax_scale, int causal, hipStream_t stream) {
+    return fwd_varlen_impl(true, q, k, v, o, lse, cu_seqlens, nseq, total, max_seqlen, H,
+                           D, softmax_scale, causal, stream);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, void* workspace,
+           size_t ws_bytes, int B, int H, int N, int D, float softmax_scale, int causal,
+           hipStream_t stream) {
+    return bwd_impl(false, q, k, v, o, lse, dout, dq, dk, dv, workspace, ws_bytes, B, H, N,
+                    D, softmax_scale, causal, stream);
+}
+int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, void* workspace,
+               size_t ws_bytes, int B, int H, int N, int D, float softmax_scale, int causal,
+               hipStream_t stream) {
+    return bwd_impl(true, q, k, v, o, lse, dout, dq, dk, dv, workspace, ws_bytes, B, H, N,
+                    D, softmax_scale, causal, stream);
 }
 
 }  // extern "C"

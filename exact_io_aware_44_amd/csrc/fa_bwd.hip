@@ -78,7 +78,7 @@ __device__ __forceinline__ void unit_of(int i, int total, int per_head, int& hea
 // 1. Per-row constants: D_i = dO_i . O_i (fp32 sum of exact bf16 products)
 //    and -L_i log2(e), the exponent offset that turns a score into its weight.
 // ---------------------------------------------------------------------------
-template <int D>
+template <typename E, int D>
 __global__ __launch_bounds__(256) void dsum_kernel(const bf16* o, const bf16* dout,
                                                    const float* lse, float* dd, float* nl2,
                                                    int64_t rows) {
@@ -91,7 +91,8 @@ __global__ __launch_bounds__(256) void dsum_kernel(const bf16* o, const bf16* do
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + row * D + part * 8);
         const bf16x8 b = *reinterpret_cast<const bf16x8*>(dout + row * D + part * 8);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc = __builtin_fmaf((float)a[j], (float)b[j], acc);
+        for (int j = 0; j < 8; ++j)
+            acc = __builtin_fmaf(to_f32<E>(a[j]), to_f32<E>(b[j]), acc);
     }
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
@@ -142,8 +143,12 @@ __device__ __forceinline__ int qd_off(int r, int chunk) {  // element offset
 //    the s_nop 1;
 //  - back-to-back accumulation into the same registers is interlocked;
 //  - reading acc after the last MFMA needs the wait of mfma_acc_drain.
+template <typename E>
 __device__ __forceinline__ void mfma_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
-    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    if constexpr (__is_same(E, f16))
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 // Wait states between the last MFMA into an accumulator and any read of it
 // (a 16-pass MFMA result needs at most 18).
@@ -151,7 +156,7 @@ __device__ __forceinline__ void mfma_acc_drain(f32x16& a, f32x16& b) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a), "+a"(b));
 }
 
-template <int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     using T = KvTile<D>;
     // one LDS object per buffer, selected statically, so the compiler can tell
@@ -229,8 +234,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int ss = 0; ss < T::DS; ++ss) {
             const int off = qd_off<D>(32 * b + l32, 2 * ss + hi);
-            s = mfma32(lds_read16(qs + off), kreg[ss], s);
-            dp = mfma32(lds_read16(dos + off), vreg[ss], dp);
+            s = mfma32<E>(lds_read16(qs + off), kreg[ss], s);
+            dp = mfma32<E>(lds_read16(dos + off), vreg[ss], dp);
         }
     };
     // P = exp2(S c - L log2 e) and dS = P (dP - D), rounded to bf16 in the
@@ -241,6 +246,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
                        __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int tm = kj - qb0 - 4 * hi;  // masked where tm > local query offset
+        float pf[16], sf[16];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             const f32x4 nl = *reinterpret_cast<const f32x4*>(fs + 32 * b + 8 * a + 4 * hi);
@@ -251,11 +257,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
                 const int r = 4 * a + x;
                 float pv = exp2_fast(__builtin_fmaf(s[r], p.c, nl[x]));
                 if (MASK) pv = tm > 8 * a + x ? 0.f : pv;
-                const float dsv = pv * (dp[r] - dd[x]);
-                pb[r / 8][r % 8] = to_bf16(pv);
-                sb[r / 8][r % 8] = to_bf16(dsv);
+                pf[r] = pv;
+                sf[r] = pv * (dp[r] - dd[x]);
             }
         }
+        pb[0] = pack8<E>(pf);
+        pb[1] = pack8<E>(pf + 8);
+        sb[0] = pack8<E>(sf);
+        sb[1] = pack8<E>(sf + 8);
     };
     // dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T by transpose reads,
     // their query order matching the B operands'.
@@ -270,9 +279,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
                 const int o0 = qd_off<D>(rr, cc) + 4 * (i16 & 1);
                 const int o1 = qd_off<D>(rr + 8, cc) + 4 * (i16 & 1);
                 const bf16x8 doT = cat(lds_read_tr(dos + o0), lds_read_tr(dos + o1));
-                mfma_acc(dv[e], doT, pb[t]);
+                mfma_acc<E>(dv[e], doT, pb[t]);
                 const bf16x8 qT = cat(lds_read_tr(qs + o0), lds_read_tr(qs + o1));
-                mfma_acc(dk[e], qT, sb[t]);
+                mfma_acc<E>(dk[e], qT, sb[t]);
             }
     };
     using True = std::true_type;
@@ -364,10 +373,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int d = 32 * e + 8 * r4 + 4 * hi;
                 const uint32_t off = ((uint32_t)kj * D + d) * 2;
-                store8(dvb, off, pack4(dv[e][4 * r4], dv[e][4 * r4 + 1],
+                store8(dvb, off, pack4<E>(dv[e][4 * r4], dv[e][4 * r4 + 1],
                                        dv[e][4 * r4 + 2], dv[e][4 * r4 + 3]));
                 store8(dkb, off,
-                       pack4(dk[e][4 * r4] * p.scale, dk[e][4 * r4 + 1] * p.scale,
+                       pack4<E>(dk[e][4 * r4] * p.scale, dk[e][4 * r4 + 1] * p.scale,
                              dk[e][4 * r4 + 2] * p.scale, dk[e][4 * r4 + 3] * p.scale));
             }
     }
@@ -393,7 +402,7 @@ struct QTile {
     static constexpr int DB = D / 32;
 };
 
-template <int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     using T = QTile<D>;
     __shared__ __attribute__((aligned(16))) bf16 k_lds0[T::T_ELEMS];
@@ -463,8 +472,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
 #pragma unroll
         for (int ss = 0; ss < T::DS; ++ss) {
             const int off = qd_off<D>(32 * b + l32, 2 * ss + hi);
-            s = mfma32(lds_read16(ks + off), qreg[ss], s);
-            dp = mfma32(lds_read16(vs + off), doreg[ss], dp);
+            s = mfma32<E>(lds_read16(ks + off), qreg[ss], s);
+            dp = mfma32<E>(lds_read16(vs + off), doreg[ss], dp);
         }
     };
     // dS^T = P^T (dP^T - D), P^T = exp2(S^T c - L log2 e), in bf16 B-operand
@@ -473,12 +482,15 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
                        auto mask_tag) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int lim = qi - kb0 - 4 * hi;  // masked where local key offset > lim
+        float sf[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float pv = exp2_fast(__builtin_fmaf(s[r], p.c, nl2));
             if (MASK) pv = 8 * (r >> 2) + (r & 3) > lim ? 0.f : pv;
-            sb[r / 8][r % 8] = to_bf16(pv * (dp[r] - dd));
+            sf[r] = pv * (dp[r] - dd);
         }
+        sb[0] = pack8<E>(sf);
+        sb[1] = pack8<E>(sf + 8);
     };
     // dQ^T += K^T dS^T with K^T by transpose reads of the row-major stage.
     auto accumulate = [&](const bf16* __restrict__ ks, int b, const bf16x8* sb)
@@ -491,7 +503,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
                 const int cc = 4 * e + 2 * (g & 1) + ((i16 & 3) >> 1);
                 const int o0 = qd_off<D>(rr, cc) + 4 * (i16 & 1);
                 const int o1 = qd_off<D>(rr + 8, cc) + 4 * (i16 & 1);
-                mfma_acc(acc[e], cat(lds_read_tr(ks + o0), lds_read_tr(ks + o1)), sb[t]);
+                mfma_acc<E>(acc[e], cat(lds_read_tr(ks + o0), lds_read_tr(ks + o1)), sb[t]);
             }
     };
     using True = std::true_type;
@@ -581,13 +593,13 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int d = 32 * e + 8 * r4 + 4 * hi;
                 store8(dqb, ((uint32_t)qi * D + d) * 2,
-                       pack4(acc[e][4 * r4] * p.scale, acc[e][4 * r4 + 1] * p.scale,
+                       pack4<E>(acc[e][4 * r4] * p.scale, acc[e][4 * r4 + 1] * p.scale,
                              acc[e][4 * r4 + 2] * p.scale, acc[e][4 * r4 + 3] * p.scale));
             }
     }
 }
 
-template <int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL>
 hipError_t run_bwd(const BwdArgs& a, hipStream_t stream) {
     BwdParams p;
     p.q = static_cast<const bf16*>(a.q);
@@ -608,7 +620,7 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream) {
     p.scale = a.scale;
 
     const int64_t threads = rows * (D / 8);
-    hipLaunchKernelGGL((dsum_kernel<D>), dim3((unsigned)((threads + 255) / 256)),
+    hipLaunchKernelGGL((dsum_kernel<E, D>), dim3((unsigned)((threads + 255) / 256)),
                        dim3(256), 0, stream, p.o, p.dout, p.lse, p.dd, p.nl2, rows);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -616,7 +628,7 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream) {
     const int nkt = (a.N + KvTile<D>::BK - 1) / KvTile<D>::BK;
     p.per_head = CAUSAL ? (nkt + 1) / 2 : nkt;
     const int64_t units = (int64_t)p.per_head * a.H * a.B;
-    hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3((unsigned)units), dim3(256), 0,
+    hipLaunchKernelGGL((dkdv_kernel<E, D, CAUSAL>), dim3((unsigned)units), dim3(256), 0,
                        stream, p);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -625,17 +637,22 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream) {
     const int nqt = (a.N + QTile<D>::BR - 1) / QTile<D>::BR;
     p.per_head = CAUSAL ? (nqt + 1) / 2 : nqt;
     const int64_t qunits = (int64_t)p.per_head * a.H * a.B;
-    hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3((unsigned)qunits), dim3(256), 0, stream,
+    hipLaunchKernelGGL((dq_kernel<E, D, CAUSAL>), dim3((unsigned)qunits), dim3(256), 0, stream,
                        p);
     return hipGetLastError();
+}
+
+template <typename E>
+hipError_t run_bwd_e(const BwdArgs& a, hipStream_t stream) {
+    if (a.D == 64)
+        return a.causal ? run_bwd<E, 64, true>(a, stream) : run_bwd<E, 64, false>(a, stream);
+    return a.causal ? run_bwd<E, 128, true>(a, stream) : run_bwd<E, 128, false>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
-    if (a.D == 64)
-        return a.causal ? run_bwd<64, true>(a, stream) : run_bwd<64, false>(a, stream);
-    return a.causal ? run_bwd<128, true>(a, stream) : run_bwd<128, false>(a, stream);
+    return a.f16 ? run_bwd_e<f16>(a, stream) : run_bwd_e<bf16>(a, stream);
 }
 
 }  // namespace fa

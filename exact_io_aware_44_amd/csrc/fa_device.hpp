@@ -26,9 +26,16 @@
 
 namespace fa {
 
+// 16-bit elements travel (global, LDS, registers) as bf16-typed vectors; the
+// element type E (bf16 or f16) only matters where they are computed with:
+// the MFMA and the rounding of fp32 values to 16 bits.
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -92,8 +99,15 @@ __device__ __forceinline__ float loadf(Buf b, uint32_t off) {
 }
 
 // ---- MFMA ------------------------------------------------------------------
+// D += A B on v_mfma_f32_32x32x16_{bf16,f16}: same shape and register layout.
+template <typename E>
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    if constexpr (__is_same(E, f16))
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0,
+                                                      0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // ---- LDS -------------------------------------------------------------------
@@ -112,7 +126,37 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
 }
 
 // ---- conversions / math ----------------------------------------------------
-__device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }  // RNE
+// Two fp32 values rounded to nearest-even 16-bit elements of type E, packed
+// (low half = a) into one dword.
+template <typename E>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    if constexpr (__is_same(E, f16))
+        return __builtin_bit_cast(uint32_t, f16x2{(f16)a, (f16)b});
+    else
+        return __builtin_bit_cast(uint32_t, bf16x2{(bf16)a, (bf16)b});
+}
+// Eight fp32 values as one MFMA operand of element type E.
+template <typename E>
+__device__ __forceinline__ bf16x8 pack8(const float* x) {
+    const u32x4 w{pack2<E>(x[0], x[1]), pack2<E>(x[2], x[3]), pack2<E>(x[4], x[5]),
+                  pack2<E>(x[6], x[7])};
+    return __builtin_bit_cast(bf16x8, w);
+}
+// Elements o .. o+7 of a score block as one MFMA operand of element type E.
+template <typename E>
+__device__ __forceinline__ bf16x8 pack8(const f32x16& x, int o) {
+    const u32x4 w{pack2<E>(x[o], x[o + 1]), pack2<E>(x[o + 2], x[o + 3]),
+                  pack2<E>(x[o + 4], x[o + 5]), pack2<E>(x[o + 6], x[o + 7])};
+    return __builtin_bit_cast(bf16x8, w);
+}
+// The value of a 16-bit element of type E.
+template <typename E>
+__device__ __forceinline__ float to_f32(bf16 raw) {
+    if constexpr (__is_same(E, f16))
+        return (float)__builtin_bit_cast(f16, raw);
+    else
+        return (float)raw;
+}
 __device__ __forceinline__ float exp2_fast(float x) {
     return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
 }
@@ -139,9 +183,9 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
+template <typename E>
 __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
-    bf16x4 v{to_bf16(a), to_bf16(b), to_bf16(c), to_bf16(d)};
-    return __builtin_bit_cast(u32x2, v);
+    return u32x2{pack2<E>(a, b), pack2<E>(c, d)};
 }
 
 }  // namespace fa

@@ -123,7 +123,7 @@ __device__ __forceinline__ void unit_of(int i, int total, int per_head, int& hea
 using True = std::true_type;
 using False = std::false_type;
 
-template <int D, bool CAUSAL, bool VARLEN, bool SPLIT>
+template <typename E, int D, bool CAUSAL, bool VARLEN, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     using T = FwdTile<D>;
     // Separate LDS objects per buffer, always selected statically, so the
@@ -289,15 +289,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         // exponentials in place, summed in fp32 in four independent chains
         // (summing the bf16-rounded weights instead would put up to 2^-9
         // relative error into l when one weight dominates and the reference
-        // maximum is stale), then packed to bf16
+        // maximum is stale), then rounded to 16-bit B operands
         float rs[4];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             s[r] = exp2_fast(__builtin_fmaf(s[r], p.c, -m_use));
             rs[r & 3] = r < 4 ? s[r] : rs[r & 3] + s[r];
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = to_bf16(s[r]);
+        pb[0] = pack8<E>(s, 0);
+        pb[1] = pack8<E>(s, 8);
         l_new = (rs[0] + rs[1]) + (rs[2] + rs[3]);  // taken against m_new
     };
     // Bring the old sums (u, and l before this half) to the new maximum, then
@@ -350,10 +350,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         };
         auto apply = [&](int i, bf16x8 a) {
             if (kind_s(i)) {
-                s_nxt = mfma32(a, qreg[MIX ? i >> 1 : i], s_nxt);
+                s_nxt = mfma32<E>(a, qreg[MIX ? i >> 1 : i], s_nxt);
             } else {
                 const int k = MIX ? i >> 1 : i;
-                acc[k % T::DB] = mfma32(a, pb_prev[k / T::DB], acc[k % T::DB]);
+                acc[k % T::DB] = mfma32<E>(a, pb_prev[k / T::DB], acc[k % T::DB]);
             }
         };
         if constexpr (DO_S) s_nxt = f32x16{};
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         bool upd;
         sA = f32x16{};
     #pragma unroll
-        for (int ss = 0; ss < T::DS; ++ss) sA = mfma32(k_op(k_lds0, 0, ss), qreg[ss], sA);
+        for (int ss = 0; ss < T::DS; ++ss) sA = mfma32<E>(k_op(k_lds0, 0, ss), qreg[ss], sA);
         if (needs_mask(0)) apply_mask(sA, 0);
         half_step(True{}, False{}, True{}, k_lds0, 1, nullptr, 0, sA, sB, pB, pA, alpha, upd);
         l_run = l_new;  // first half: nothing to rescale
@@ -447,7 +447,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
                 store16(pob, ((uint32_t)qi * D + d) * 4, __builtin_bit_cast(u32x4, ov));
             } else {
                 store8(ob, ((uint32_t)qi * D + d) * 2,
-                       pack4(acc[e][4 * r4] * inv, acc[e][4 * r4 + 1] * inv,
+                       pack4<E>(acc[e][4 * r4] * inv, acc[e][4 * r4 + 1] * inv,
                              acc[e][4 * r4 + 2] * inv, acc[e][4 * r4 + 3] * inv));
             }
         }
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 // Split key ranges, second step: per query row, L = ln sum_s exp(L_s) and
 // O = sum_s exp(L_s - L) O_s (the running-softmax rule of tensortonic
 // section 5 applied to whole key ranges).  One thread per 4 output columns.
-template <int D>
+template <typename E, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const float* part_o, const float* part_l,
                                                     bf16* o, float* lse, int64_t rows,
                                                     int splits) {
@@ -482,11 +482,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* part_o, const f
         }
         L = m + log2_fast(sum) * kLn2;
     }
-    *reinterpret_cast<u32x2*>(o + row * D + 4 * c) = pack4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<u32x2*>(o + row * D + 4 * c) = pack4<E>(acc[0], acc[1], acc[2], acc[3]);
     if (lse && c == 0) lse[row] = L;
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool SPLIT>
+template <typename E, int D, bool CAUSAL, bool VARLEN, bool SPLIT>
 hipError_t run_fwd(const FwdArgs& a, hipStream_t stream) {
     using T = FwdTile<D>;
     FwdParams p;
@@ -509,34 +509,35 @@ hipError_t run_fwd(const FwdArgs& a, hipStream_t stream) {
     p.part_o = a.part;
     p.part_l = a.part + ((rows * a.splits * D + 63) & ~(int64_t)63);
     const int64_t units = (int64_t)p.per_head * a.H * a.B;
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, VARLEN, SPLIT>), dim3((unsigned)units),
+    hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, VARLEN, SPLIT>), dim3((unsigned)units),
                        dim3(T::THREADS), 0, stream, p);
     if (!SPLIT) return hipGetLastError();
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t threads = rows * (D / 4);
-    hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
+    hipLaunchKernelGGL((merge_kernel<E, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
                        0, stream, p.part_o, p.part_l, p.o, p.lse, rows, a.splits);
     return hipGetLastError();
 }
 
-template <int D>
+template <typename E, int D>
 hipError_t run_fwd_d(const FwdArgs& a, hipStream_t stream) {
     const bool varlen = a.cu != nullptr;
     if (a.splits > 1)
-        return a.causal ? run_fwd<D, true, false, true>(a, stream)
-                        : run_fwd<D, false, false, true>(a, stream);
+        return a.causal ? run_fwd<E, D, true, false, true>(a, stream)
+                        : run_fwd<E, D, false, false, true>(a, stream);
     if (a.causal)
-        return varlen ? run_fwd<D, true, true, false>(a, stream)
-                      : run_fwd<D, true, false, false>(a, stream);
-    return varlen ? run_fwd<D, false, true, false>(a, stream)
-                  : run_fwd<D, false, false, false>(a, stream);
+        return varlen ? run_fwd<E, D, true, true, false>(a, stream)
+                      : run_fwd<E, D, true, false, false>(a, stream);
+    return varlen ? run_fwd<E, D, false, true, false>(a, stream)
+                  : run_fwd<E, D, false, false, false>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-    return a.D == 64 ? run_fwd_d<64>(a, stream) : run_fwd_d<128>(a, stream);
+    if (a.f16) return a.D == 64 ? run_fwd_d<f16, 64>(a, stream) : run_fwd_d<f16, 128>(a, stream);
+    return a.D == 64 ? run_fwd_d<bf16, 64>(a, stream) : run_fwd_d<bf16, 128>(a, stream);
 }
 
 }  // namespace fa

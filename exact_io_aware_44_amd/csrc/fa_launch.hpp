@@ -26,6 +26,7 @@ struct FwdArgs {
     int splits = 1;         // > 1: key ranges split across units (dense only)
     int chunk = 0;          // keys per split, a multiple of 64
     float* part = nullptr;  // split workspace: partial O, then partial L (fp32)
+    bool f16 = false;       // element type: bf16, or fp16 when set
 };
 
 struct BwdArgs {
@@ -43,6 +44,7 @@ struct BwdArgs {
     int B, H, N, D;
     float scale;
     bool causal;
+    bool f16 = false;       // element type: bf16, or fp16 when set
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);

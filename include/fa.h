@@ -13,11 +13,12 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Element types: q, k, v, o, dout, dq, dk, dv are bfloat16 (raw 16-bit
- *    storage, round-to-nearest-even on output); lse is float32.  Arithmetic
- *    is bf16 x bf16 products with float32 accumulation.
+ *    storage, round-to-nearest-even on output) -- or IEEE fp16 for the *_f16
+ *    variants at the end; lse is float32.  Arithmetic is 16-bit x 16-bit
+ *    products with float32 accumulation.
  *  - Dense layout: [B, H, N, D] row-major, contiguous (tensortonic section 9:
  *    [batch, heads, tokens, head_width]); lse is [B, H, N].  Q, K and V have
- *    the same length N.
+ *    the same length N, except in fa_fwd_qk and fa_fwd_splitkv.
  *  - Causal masking (causal = 1) lets query i read keys j <= i (a token reads
  *    itself and the past, never the future: tensortonic section 1).
  *  - softmax_scale multiplies the float32 dot product q_i . k_j before the
@@ -197,6 +198,32 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dout, void* dq, void* dk, void* dv,
            void* workspace, size_t workspace_bytes, int B, int H, int N, int D,
            float softmax_scale, int causal, hipStream_t stream);
+
+/*
+ * FP16 variants (nexusofnerds "What is FlashAttention?": the kernels run in
+ * mixed precision with BF16 or FP16 inputs).  Each has the contract of the
+ * function without the suffix, with every 16-bit tensor (q, k, v, o, dout,
+ * dq, dk, dv) in IEEE binary16 instead of bfloat16; the scores, softmax
+ * statistics, accumulators, lse and workspaces stay fp32, and the 16-bit
+ * results are rounded to nearest-even.  The workspace sizes are those of
+ * fa_fwd_splitkv_workspace_size and fa_bwd_workspace_size.
+ */
+int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+               int H, int N, int D, float softmax_scale, int causal, hipStream_t stream);
+int fa_fwd_qk_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                  int H, int Nq, int Nk, int D, float softmax_scale, int causal,
+                  hipStream_t stream);
+int fa_fwd_splitkv_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                       void* workspace, size_t workspace_bytes, int B, int H, int Nq,
+                       int Nk, int D, float softmax_scale, int causal, int num_splits,
+                       hipStream_t stream);
+int fa_fwd_varlen_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int32_t* cu_seqlens, int nseq, int total, int max_seqlen,
+                      int H, int D, float softmax_scale, int causal, hipStream_t stream);
+int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, void* workspace,
+               size_t workspace_bytes, int B, int H, int N, int D, float softmax_scale,
+               int causal, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_string(int status);

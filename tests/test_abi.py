@@ -30,14 +30,15 @@ def lib():
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert names == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_qk",
-                     "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
-                     "fa_fwd_varlen", "fa_status_string"]
+    assert names == ["fa_bwd", "fa_bwd_f16", "fa_bwd_workspace_size", "fa_fwd",
+                     "fa_fwd_f16", "fa_fwd_qk", "fa_fwd_qk_f16", "fa_fwd_splitkv",
+                     "fa_fwd_splitkv_f16", "fa_fwd_splitkv_workspace_size",
+                     "fa_fwd_varlen", "fa_fwd_varlen_f16", "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -173,3 +174,31 @@ def test_python_binding_checks_dtypes():
     y = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fa_fwd(y, y, y)  # CPU tensors are refused: no CPU fallback
+    z = torch.zeros(1, 1, 4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(z, z, z)  # fp16 is accepted as a type, CPU still refused
+
+
+@pytest.mark.parametrize("name", ["fa_fwd", "fa_fwd_qk", "fa_fwd_splitkv",
+                                  "fa_fwd_varlen", "fa_bwd"])
+def test_f16_twins_validate_like_bf16(lib, name):
+    """The fp16 entry points share the validation of their bf16 twins: the
+    same argument list with one invalid value gets the same status."""
+    calls = {
+        "fa_fwd": lambda f, **kw: f(*[kw.get(n, d) for n, d in (
+            ("q", P), ("k", P), ("v", P), ("o", P), ("lse", P), ("B", 1), ("H", 1),
+            ("N", 16), ("D", 64), ("s", 0.125), ("c", 0))], None),
+        "fa_fwd_qk": lambda f, **kw: f(P, P, P, P, P, 1, 1, 16, kw.get("Nk", 40),
+                                       kw.get("D", 64), 0.125, 1, None),
+        "fa_fwd_splitkv": lambda f, **kw: f(P, P, P, P, P, kw.get("ws", P), 1 << 30, 2, 4, 1,
+                                            4096, kw.get("D", 128), 0.1, 1, 0, None),
+        "fa_fwd_varlen": lambda f, **kw: f(P, P, P, P, P, kw.get("cu", P), 2, 32, 16, 2,
+                                           kw.get("D", 128), 0.1, 1, None),
+        "fa_bwd": lambda f, **kw: f(P, P, P, P, P, P, P, P, P, kw.get("ws", P), 1 << 30, 1, 2,
+                                    64, kw.get("D", 128), 0.1, 1, None),
+    }
+    call = calls[name]
+    bf, hf = getattr(lib, name), getattr(lib, name + "_f16")
+    for kw, code in ((dict(D=96), UNSUP), (dict(q=None) if name == "fa_fwd" else dict(D=0), None)):
+        a, b = call(bf, **kw), call(hf, **kw)
+        assert a == b and a != OK and (code is None or a == code)
