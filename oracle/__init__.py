@@ -70,6 +70,23 @@ def _load():
     lib.oracle_attn_fwd_qk_rows.argtypes = [_D, _D, _D, _I64, _I64, _i64, _D, _D,
                                             _i64, _i64, _i64, _i64, _i64,
                                             ctypes.c_double, ctypes.c_int]
+    _u32p = ctypes.POINTER(ctypes.c_uint32)
+    _u64 = ctypes.c_uint64
+    lib.oracle_philox4x32_10.argtypes = [_u32p, _u32p, _u32p]
+    lib.oracle_philox4x32_10.restype = None
+    lib.oracle_dropout_threshold.argtypes = [ctypes.c_double]
+    lib.oracle_dropout_threshold.restype = ctypes.c_int
+    lib.oracle_dropout_mask.argtypes = [ctypes.POINTER(ctypes.c_uint8), _i64, _i64, _i64,
+                                        ctypes.c_double, _u64, _u64]
+    lib.oracle_attn_fwd_dropout.argtypes = [_D, _D, _D, _D, _D, _i64, _i64, _i64, _i64,
+                                            ctypes.c_double, ctypes.c_int, ctypes.c_double,
+                                            _u64, _u64]
+    lib.oracle_attn_bwd_dropout.argtypes = [_D, _D, _D, _D, _D, _D, _D, _i64, _i64, _i64,
+                                            _i64, ctypes.c_double, ctypes.c_int,
+                                            ctypes.c_double, _u64, _u64]
+    for f in (lib.oracle_dropout_mask, lib.oracle_attn_fwd_dropout,
+              lib.oracle_attn_bwd_dropout):
+        f.restype = ctypes.c_int
     lib.oracle_attn_bwd.argtypes = [_D, _D, _D, _D, _D, _D, _D, _i64, _i64,
                                     _i64, _i64, ctypes.c_double, ctypes.c_int]
     for f in (lib.oracle_attn_fwd, lib.oracle_attn_fwd_rows,
@@ -221,3 +238,56 @@ def _i32(x) -> np.ndarray:
     if hasattr(x, "detach"):
         x = x.detach().cpu().numpy()
     return np.asarray(x, dtype=np.int32)
+
+
+# ---------------------------------------------------------------------------
+# Dropout
+# ---------------------------------------------------------------------------
+def philox4x32_10(counter, key):
+    """One Philox4x32-10 call: four uint32 counter words, two key words."""
+    c = np.ascontiguousarray(counter, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.empty(4, dtype=np.uint32)
+    u32 = ctypes.POINTER(ctypes.c_uint32)
+    _load().oracle_philox4x32_10(c.ctypes.data_as(u32), k.ctypes.data_as(u32),
+                                 out.ctypes.data_as(u32))
+    return out
+
+
+def dropout_threshold(p: float) -> int:
+    """T with keep iff decision byte >= T (dropout probability T / 256)."""
+    return int(_load().oracle_dropout_threshold(float(p)))
+
+
+def dropout_mask(bh: int, nq: int, nk: int, p: float, seed: int, offset: int):
+    """Keep mask (bool [nq, nk]) of flattened head bh."""
+    keep = np.empty((nq, nk), dtype=np.uint8)
+    _check(_load().oracle_dropout_mask(keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                       bh, nq, nk, float(p), int(seed), int(offset)),
+           "dropout_mask")
+    return keep.astype(bool)
+
+
+def fwd_dropout(q, k, v, scale: float, causal: bool, p: float, seed: int, offset: int):
+    """Dense forward with attention dropout.  Returns (O, L)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, D = q.shape
+    o = np.empty_like(q)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    _check(_load().oracle_attn_fwd_dropout(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, N, D,
+                                           float(scale), int(bool(causal)), float(p),
+                                           int(seed), int(offset)), "fwd_dropout")
+    return o, lse
+
+
+def bwd_dropout(q, k, v, dout, scale: float, causal: bool, p: float, seed: int,
+                offset: int):
+    """Dense backward with attention dropout (same decisions as fwd_dropout)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, D = q.shape
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    _check(_load().oracle_attn_bwd_dropout(_p(q), _p(k), _p(v), _p(dout), _p(dq), _p(dk),
+                                           _p(dv), B, H, N, D, float(scale),
+                                           int(bool(causal)), float(p), int(seed),
+                                           int(offset)), "bwd_dropout")
+    return dq, dk, dv

@@ -55,6 +55,30 @@
  * attention crosses a sequence boundary (nexusofnerds: variable-length
  * packing).
  *
+ * Attention dropout (tensortonic section 7: with dropout enabled the backward
+ * pass must reproduce the forward pass's drop decisions from saved generator
+ * state; it may not draw a new mask).  The weights become
+ * P~_ij = P_ij * keep_ij / (1 - p'), O_i = sum_j P~_ij v_j, while L keeps the
+ * log-sum-exp of the undropped scores.  The pages fix no generator, so this
+ * library defines the decisions (a reading, listed in the design doc) with the
+ * counter-based generator Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011), implemented below
+ * from that paper's definition:
+ *   - one call maps a 128-bit counter (c0, c1, c2, c3) and a 64-bit key
+ *     (k0, k1) to 128 bits through ten rounds; a round forms the 64-bit
+ *     products 0xD2511F53 * c0 = (hi0, lo0) and 0xCD9E8D57 * c2 = (hi1, lo1)
+ *     and yields (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); between rounds
+ *     the key advances by (0x9E3779B9, 0xBB67AE85);
+ *   - query i and key j of head bh (= b*H + h) use the call with counter
+ *     (j / 4, i / 4, bh, offset mod 2^32) and key (seed mod 2^32,
+ *     seed / 2^32); byte j % 4 of output word i % 4 is u;
+ *   - key j is kept for query i iff u >= T, T = min(255, round(256 p)), so
+ *     the dropout probability is p' = T / 256 and kept weights are scaled by
+ *     256 / (256 - T).
+ * The generator's output stream is parity unpinned against other
+ * implementations (no reference vectors are used); the tests pin its
+ * statistics and every use of it.
+ *
  * Build: gcc -O2 -fopenmp -fPIC -shared oracle.c -lm   (no -ffast-math).
  */
 #include <math.h>
@@ -416,4 +440,208 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v,
     free(P);
     free(dS);
     return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Dropout: the counter-based generator and the attention with dropped weights.
+ * ------------------------------------------------------------------------- */
+
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+    uint32_t c[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = lo1;
+        c[2] = n2;
+        c[3] = lo0;
+    }
+    out[0] = c[0];
+    out[1] = c[1];
+    out[2] = c[2];
+    out[3] = c[3];
+}
+
+/* The drop threshold T for probability p (keep iff the decision byte >= T). */
+int oracle_dropout_threshold(double p) {
+    if (!(p > 0.0)) return 0;
+    const double t = floor(p * 256.0 + 0.5);
+    return t > 255.0 ? 255 : (int)t;
+}
+
+/* keep_ij of query i and key j of head bh (1 = kept). */
+static int keep_bit(uint64_t seed, uint64_t offset, int64_t bh, int64_t i, int64_t j,
+                    int T) {
+    if (T == 0) return 1;
+    const uint32_t ctr[4] = {(uint32_t)(j >> 2), (uint32_t)(i >> 2), (uint32_t)bh,
+                             (uint32_t)offset};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    oracle_philox4x32_10(ctr, key, out);
+    const uint32_t u = (out[i & 3] >> (8 * (j & 3))) & 0xFFu;
+    return u >= (uint32_t)T;
+}
+
+/* The keep mask of head bh for rows [0, nq) and keys [0, nk): keep[i*nk + j]. */
+int oracle_dropout_mask(uint8_t* keep, int64_t bh, int64_t nq, int64_t nk, double p,
+                        uint64_t seed, uint64_t offset) {
+    if (nq < 0 || nk < 0 || !(p >= 0.0 && p < 1.0)) return 1;
+    const int T = oracle_dropout_threshold(p);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nq; ++i)
+        for (int64_t j = 0; j < nk; ++j)
+            keep[i * nk + j] = (uint8_t)keep_bit(seed, offset, bh, i, j, T);
+    return 0;
+}
+
+/* Dense forward with dropout: O_i = sum_j P_ij keep_ij / (1 - p') v_j;
+ * L_i = m_i + ln l_i of the undropped scores. */
+int oracle_attn_fwd_dropout(const double* q, const double* k, const double* v, double* o,
+                            double* lse, int64_t B, int64_t H, int64_t N, int64_t D,
+                            double scale, int causal, double p, uint64_t seed,
+                            uint64_t offset) {
+    if (B < 0 || H < 0 || N < 0 || D <= 0 || !(p >= 0.0 && p < 1.0)) return 1;
+    const int T = oracle_dropout_threshold(p);
+    const double inv_keep = 256.0 / (256.0 - T);
+    const int64_t rows = B * H * N;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < rows; ++r) {
+                const int64_t bh = r / N, i = r % N, base = bh * N * D;
+                const double* q_i = q + base + i * D;
+                double* o_i = o + base + i * D;
+                const int64_t nk = allowed_keys(i, N, causal);
+                for (int64_t d = 0; d < D; ++d) o_i[d] = 0.0;
+                double m = -INFINITY, l = 0.0;
+                for (int64_t j = 0; j < nk; ++j) {
+                    s[j] = scale * dot(q_i, k + base + j * D, D);
+                    if (s[j] > m) m = s[j];
+                }
+                for (int64_t j = 0; j < nk; ++j) {
+                    s[j] = exp(s[j] - m);
+                    l += s[j];
+                }
+                for (int64_t j = 0; j < nk; ++j) {
+                    if (!keep_bit(seed, offset, bh, i, j, T)) continue;
+                    const double w = s[j] / l * inv_keep;
+                    const double* v_j = v + base + j * D;
+                    for (int64_t d = 0; d < D; ++d) o_i[d] += w * v_j[d];
+                }
+                lse[bh * N + i] = nk > 0 ? m + log(l) : -INFINITY;
+            }
+            free(s);
+        }
+    }
+    return fail;
+}
+
+/*
+ * Backward with dropout: the exact vector-Jacobian product of
+ * oracle_attn_fwd_dropout with the same decisions.  With Z_ij = keep_ij /
+ * (1 - p') and G_ij = <dO_i, v_j>:
+ *   dV_j = sum_i P_ij Z_ij dO_i,   dP_ij = G_ij Z_ij,
+ *   dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik),
+ *   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i.
+ */
+int oracle_attn_bwd_dropout(const double* q, const double* k, const double* v,
+                            const double* dout, double* dq, double* dk, double* dv,
+                            int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                            int causal, double p, uint64_t seed, uint64_t offset) {
+    if (B < 0 || H < 0 || N < 0 || D <= 0 || !(p >= 0.0 && p < 1.0)) return 1;
+    if (N == 0) return 0;
+    const int T = oracle_dropout_threshold(p);
+    const double inv_keep = 256.0 / (256.0 - T);
+    double* PZ = (double*)malloc(sizeof(double) * (size_t)(N * N));  /* P_ij Z_ij */
+    double* dS = (double*)malloc(sizeof(double) * (size_t)(N * N));
+    if (!PZ || !dS) {
+        free(PZ);
+        free(dS);
+        return 1;
+    }
+    int fail = 0;
+    for (int64_t bh = 0; bh < B * H && !fail; ++bh) {
+        const int64_t base = bh * N * D;
+        const double *qh = q + base, *kh = k + base, *vh = v + base;
+        const double* doh = dout + base;
+        double *dqh = dq + base, *dkh = dk + base, *dvh = dv + base;
+#pragma omp parallel
+        {
+            double* pr = (double*)malloc(sizeof(double) * (size_t)N);   /* P_i.  */
+            double* dpr = (double*)malloc(sizeof(double) * (size_t)N);  /* dP_i. */
+            if (!pr || !dpr) {
+#pragma omp atomic write
+                fail = 1;
+            } else {
+#pragma omp for schedule(dynamic, 4)
+                for (int64_t i = 0; i < N; ++i) {
+                    const int64_t nk = allowed_keys(i, N, causal);
+                    /* forward weights of row i */
+                    double m = -INFINITY, l = 0.0;
+                    for (int64_t j = 0; j < nk; ++j) {
+                        pr[j] = scale * dot(qh + i * D, kh + j * D, D);
+                        if (pr[j] > m) m = pr[j];
+                    }
+                    for (int64_t j = 0; j < nk; ++j) {
+                        pr[j] = exp(pr[j] - m);
+                        l += pr[j];
+                    }
+                    /* dP_ij = <dO_i, v_j> Z_ij;  dsum = sum_j P_ij dP_ij */
+                    double dsum = 0.0;
+                    for (int64_t j = 0; j < nk; ++j) {
+                        pr[j] /= l;
+                        const double z =
+                            keep_bit(seed, offset, bh, i, j, T) ? inv_keep : 0.0;
+                        dpr[j] = dot(doh + i * D, vh + j * D, D) * z;
+                        PZ[i * N + j] = pr[j] * z;
+                        dsum += pr[j] * dpr[j];
+                    }
+                    for (int64_t j = 0; j < N; ++j) {
+                        dS[i * N + j] = j < nk ? pr[j] * (dpr[j] - dsum) : 0.0;
+                        if (j >= nk) PZ[i * N + j] = 0.0;
+                    }
+                    /* dQ_i = scale * sum_j dS_ij k_j */
+                    for (int64_t d = 0; d < D; ++d) dqh[i * D + d] = 0.0;
+                    for (int64_t j = 0; j < nk; ++j)
+                        for (int64_t d = 0; d < D; ++d)
+                            dqh[i * D + d] += scale * dS[i * N + j] * kh[j * D + d];
+                }
+            }
+            free(pr);
+            free(dpr);
+        }
+        if (fail) break;
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t j = 0; j < N; ++j) {
+            /* dV_j = sum_i P_ij Z_ij dO_i ;  dK_j = scale * sum_i dS_ij q_i */
+            for (int64_t d = 0; d < D; ++d) {
+                dvh[j * D + d] = 0.0;
+                dkh[j * D + d] = 0.0;
+            }
+            for (int64_t i = causal ? j : 0; i < N; ++i) {
+                const double pz = PZ[i * N + j], dsij = dS[i * N + j];
+                for (int64_t d = 0; d < D; ++d) {
+                    dvh[j * D + d] += pz * doh[i * D + d];
+                    dkh[j * D + d] += scale * dsij * qh[i * D + d];
+                }
+            }
+        }
+    }
+    free(PZ);
+    free(dS);
+    return fail;
 }

@@ -462,3 +462,91 @@ def test_key_split_partials_merge_by_lse():
     L = scipy.special.logsumexp(np.stack([p[1] for p in parts]), axis=0)
     O = sum(np.exp(p[1] - L)[..., None] * p[0] for p in parts)
     assert np.abs(L - lse).max() < 1e-13 and np.abs(O - o).max() < 1e-13
+
+
+# --------------------------------------------------------------------------
+# Attention dropout (tensortonic section 7: the backward replays the forward's
+# drop decisions).  The generator is this library's definition (Philox4x32-10
+# as published by Salmon et al.); its stream is pinned by its statistics, and
+# every use of it by closed forms and library routines on the same mask.
+# --------------------------------------------------------------------------
+def test_philox_statistics_and_injectivity():
+    outs = np.array([oracle.philox4x32_10([c, 7, 3, 0], [11, 22]) for c in range(4096)],
+                    dtype=np.uint64)
+    bits = np.array([(outs >> b) & 1 for b in range(32)], dtype=float)  # [32, 4096, 4]
+    frac = bits.mean(axis=(1, 2))
+    n = outs.size
+    assert np.abs(frac - 0.5).max() < 5 * 0.5 / math.sqrt(n)        # every bit balanced
+    by = np.concatenate([(outs >> (8 * t)) & 0xFF for t in range(4)]).ravel()
+    hist = np.bincount(by.astype(np.int64), minlength=256)
+    chi2 = ((hist - by.size / 256) ** 2 / (by.size / 256)).sum()
+    assert chi2 < 255 + 6 * math.sqrt(2 * 255)                       # bytes uniform
+    u = outs.astype(float) / 2.0 ** 32
+    assert abs(np.corrcoef(u[:-1, 0], u[1:, 0])[0, 1]) < 5 / math.sqrt(4096)
+    assert abs(np.corrcoef(u[:, 0], u[:, 1])[0, 1]) < 5 / math.sqrt(4096)
+    words = {tuple(o) for o in outs.tolist()}
+    assert len(words) == 4096                                         # no collisions
+    assert not np.array_equal(oracle.philox4x32_10([5, 7, 3, 0], [11, 22]),
+                              oracle.philox4x32_10([5, 7, 3, 0], [12, 22]))
+
+
+def test_dropout_threshold_and_mask_structure():
+    assert [oracle.dropout_threshold(p) for p in (0.0, 1 / 512, 0.1, 0.25, 0.999)] == \
+        [0, 1, 26, 64, 255]
+    big = oracle.dropout_mask(3, 100, 100, 0.3, 77, 5)
+    assert np.array_equal(oracle.dropout_mask(3, 64, 64, 0.3, 77, 5), big[:64, :64])
+    assert not np.array_equal(oracle.dropout_mask(4, 64, 64, 0.3, 77, 5), big[:64, :64])
+    assert not np.array_equal(oracle.dropout_mask(3, 64, 64, 0.3, 78, 5), big[:64, :64])
+    assert not np.array_equal(oracle.dropout_mask(3, 64, 64, 0.3, 77, 6), big[:64, :64])
+    assert oracle.dropout_mask(3, 64, 64, 0.0, 77, 5).all()
+    m = oracle.dropout_mask(0, 256, 2048, 0.3, 9, 0)
+    keep = 1 - oracle.dropout_threshold(0.3) / 256
+    assert abs(m.mean() - keep) < 5 * math.sqrt(keep * (1 - keep) / m.size)
+
+
+def _masked_reference(q, k, v, scale, causal, p, seed, offset):
+    """torch fp64: O = (softmax(S) * keep / (1 - p')) V, per head, with the
+    oracle's mask, plus autograd gradients of <dO, O>."""
+    B, H, N, D = q.shape
+    keep = np.stack([oracle.dropout_mask(bh, N, N, p, seed, offset) for bh in range(B * H)])
+    z = torch.tensor(keep.reshape(B, H, N, N), dtype=torch.float64) * \
+        (256 / (256 - oracle.dropout_threshold(p)))
+    qt, kt, vt = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    s = scale * qt @ kt.transpose(-1, -2)
+    if causal:
+        s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), -math.inf)
+    o = (torch.softmax(s, dim=-1) * z) @ vt
+    return o, torch.logsumexp(s, dim=-1), (qt, kt, vt)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_forward_backward_match_torch_on_the_same_mask(causal):
+    B, H, N, D = 2, 2, 37, 8
+    q, k, v, do = (_rand((B, H, N, D), s) for s in (50, 51, 52, 53))
+    scale, p, seed, offset = 0.4, 0.3, 1234, 99
+    o, lse = oracle.fwd_dropout(q, k, v, scale, causal, p, seed, offset)
+    o_ref, l_ref, leaves = _masked_reference(q, k, v, scale, causal, p, seed, offset)
+    assert np.abs(o - o_ref.detach().numpy()).max() < 1e-12
+    assert np.abs(lse - l_ref.detach().numpy()).max() < 1e-12
+    (o_ref * torch.tensor(do)).sum().backward()
+    grads = oracle.bwd_dropout(q, k, v, do, scale, causal, p, seed, offset)
+    for g, leaf in zip(grads, leaves):
+        assert np.abs(g - leaf.grad.numpy()).max() < 1e-12
+    # p = 0 is attention without dropout, bit for bit
+    o0, l0 = oracle.fwd_dropout(q, k, v, scale, causal, 0.0, seed, offset)
+    a, b = oracle.fwd(q, k, v, scale, causal)
+    assert np.array_equal(o0, a) and np.array_equal(l0, b)
+    g0 = oracle.bwd_dropout(q, k, v, do, scale, causal, 0.0, seed, offset)
+    for x, y in zip(g0, oracle.bwd(q, k, v, do, scale, causal)):
+        assert np.array_equal(x, y)
+
+
+def test_dropout_is_unbiased():
+    """Kept weights are scaled by 1 / (1 - p'): averaged over seeds the output
+    approaches the output without dropout."""
+    q, k, v = (_rand((1, 1, 8, 4), s) for s in (60, 61, 62))
+    ref, _ = oracle.fwd(q, k, v, 0.5, False)
+    runs = np.stack([oracle.fwd_dropout(q, k, v, 0.5, False, 0.4, seed, 0)[0]
+                     for seed in range(3000)])
+    mean, se = runs.mean(axis=0), runs.std(axis=0) / math.sqrt(len(runs))
+    assert (np.abs(mean - ref) < 5 * se + 1e-12).all()
