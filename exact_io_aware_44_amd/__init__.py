@@ -68,7 +68,16 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd.restype = _i
     lib.fa_status_string.argtypes = [_i]
     lib.fa_status_string.restype = ctypes.c_char_p
-    for name in ("fa_fwd", "fa_fwd_qk", "fa_fwd_splitkv", "fa_fwd_varlen", "fa_bwd"):
+    _u64 = ctypes.c_uint64
+    lib.fa_fwd_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _f, _u64,
+                                   _u64, _vp]
+    lib.fa_fwd_dropout.restype = _i
+    lib.fa_bwd_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   ctypes.c_size_t, _i, _i, _i, _i, _f, _i, _f, _u64, _u64,
+                                   _vp]
+    lib.fa_bwd_dropout.restype = _i
+    for name in ("fa_fwd", "fa_fwd_qk", "fa_fwd_splitkv", "fa_fwd_varlen", "fa_bwd",
+                 "fa_fwd_dropout", "fa_bwd_dropout"):
         f16 = getattr(lib, name + "_f16")  # the fp16 twin: same arguments
         f16.argtypes = getattr(lib, name).argtypes
         f16.restype = _i
@@ -128,12 +137,14 @@ def _scale(scale, D):
 
 
 def fa_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None,
-           return_lse=True, stream=None):
-    """Forward pass.  q, k, v: bf16 [B, H, N, D] on the GPU.
+           return_lse=True, stream=None, dropout_p=0.0, seed=0, offset=0):
+    """Forward pass.  q, k, v: bf16 or fp16 [B, H, N, D] on the GPU.
 
-    Returns (o, lse): o bf16 [B, H, N, D] and lse fp32 [B, H, N] (natural-log
-    row log-sum-exp of the scaled scores), or (o, None) with
-    ``return_lse=False``.  ``softmax_scale`` defaults to 1/sqrt(D).
+    Returns (o, lse): o [B, H, N, D] in q's type and lse fp32 [B, H, N]
+    (natural-log row log-sum-exp of the scaled scores), or (o, None) with
+    ``return_lse=False``.  ``softmax_scale`` defaults to 1/sqrt(D).  With
+    ``dropout_p`` > 0 the weights are dropped by fa_fwd_dropout's rule, the
+    decisions fixed by (``seed``, ``offset``): pass the same to fa_bwd.
     """
     torch = _torch()
     _check(q, "q")
@@ -147,8 +158,14 @@ def fa_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None,
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
                             or not lse.is_contiguous()):
         raise ValueError("lse must be contiguous float32 [B, H, N]")
-    rc = _fn("fa_fwd", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, D,
-                       _scale(softmax_scale, D), int(bool(causal)), _stream(stream))
+    if dropout_p:
+        rc = _fn("fa_fwd_dropout", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N,
+                                      D, _scale(softmax_scale, D), int(bool(causal)),
+                                      float(dropout_p), int(seed), int(offset),
+                                      _stream(stream))
+    else:
+        rc = _fn("fa_fwd", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, D,
+                              _scale(softmax_scale, D), int(bool(causal)), _stream(stream))
     if rc != 0:
         raise FaError(rc, "fa_fwd")
     return o, lse
@@ -254,8 +271,10 @@ def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None,
 
 
 def fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None,
-           dk=None, dv=None, workspace=None, stream=None):
-    """Backward pass.  o and lse must come from fa_fwd on the same inputs.
+           dk=None, dv=None, workspace=None, stream=None, dropout_p=0.0, seed=0, offset=0):
+    """Backward pass.  o and lse must come from fa_fwd on the same inputs (and
+    the same ``dropout_p``, ``seed`` and ``offset``, whose decisions are
+    replayed).
 
     Returns (dq, dk, dv) [B, H, N, D] in q's element type.  ``workspace`` (uint8 GPU tensor
     of at least fa_bwd_workspace_size bytes) is allocated when not given.
@@ -274,10 +293,20 @@ def fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None,
     ws_bytes = fa_bwd_workspace_size(B, H, N, D)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-    rc = _fn("fa_bwd", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
-                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                       workspace.numel() * workspace.element_size(), B, H, N, D,
-                       _scale(softmax_scale, D), int(bool(causal)), _stream(stream))
+    if dropout_p:
+        rc = _fn("fa_bwd_dropout", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                      _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                      _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), B, H,
+                                      N, D,
+                                      _scale(softmax_scale, D), int(bool(causal)),
+                                      float(dropout_p), int(seed), int(offset),
+                                      _stream(stream))
+    else:
+        rc = _fn("fa_bwd", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), B, H, N, D,
+                              _scale(softmax_scale, D), int(bool(causal)), _stream(stream))
     if rc != 0:
         raise FaError(rc, "fa_bwd")
     return dq, dk, dv

@@ -79,12 +79,26 @@ size_t splitkv_bytes(int B, int H, int Nq, int D, int splits) {
 
 // ---- the entry points, parameterised by the element type (bf16 / fp16) ----
 
+// Drop threshold T = min(255, round(256 p)) and the kept-weight scale, or an
+// error for p outside [0, 1).
+int make_dropout(float p, uint64_t seed, uint64_t offset, fa::Dropout& d) {
+    if (!std::isfinite(p) || p < 0.f || !(p < 1.f)) return FA_ERR_ARG;
+    const double t = std::floor((double)p * 256.0 + 0.5);
+    d.thresh = t > 255.0 ? 255u : (uint32_t)t;
+    d.inv_keep = (float)(256.0 / (256.0 - d.thresh));
+    d.seed_lo = (uint32_t)seed;
+    d.seed_hi = (uint32_t)(seed >> 32);
+    d.offset = (uint32_t)offset;
+    return FA_OK;
+}
+
 int fwd_impl(bool f16, const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int N, int D, float softmax_scale, int causal,
-             hipStream_t stream) {
+             hipStream_t stream, const fa::Dropout* drop = nullptr) {
     if (int rc = validate_fwd(q, k, v, o, lse, B, H, N, D, softmax_scale, causal))
         return rc;
     fa::FwdArgs a{q, k, v, o, lse, nullptr, B, H, N, N, D, softmax_scale, causal != 0, N};
+    if (drop) a.drop = *drop;
     a.f16 = f16;
     return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -147,7 +161,8 @@ int fwd_varlen_impl(bool f16, const void* q, const void* k, const void* v, void*
 int bwd_impl(bool f16, const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dout, void* dq, void* dk, void* dv,
              void* workspace, size_t ws_bytes, int B, int H, int N, int D,
-             float softmax_scale, int causal, hipStream_t stream) {
+             float softmax_scale, int causal, hipStream_t stream,
+             const fa::Dropout* drop = nullptr) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
     if (B < 1 || N < 1) return FA_ERR_SHAPE;
     if (int rc = check_common(H, D, softmax_scale, causal)) return rc;
@@ -161,6 +176,7 @@ int bwd_impl(bool f16, const void* q, const void* k, const void* v, const void* 
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
     fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace),
                   B, H, N, D, softmax_scale, causal != 0};
+    if (drop) a.drop = *drop;
     a.f16 = f16;
     return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -183,7 +199,8 @@ const char* fa_status_string(int status) {
                    "*_workspace_size function returns";
         case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: a kernel launch failed";
         case FA_ERR_ARG:
-            return "FA_ERR_ARG: softmax_scale must be finite and > 0, num_splits >= 0";
+            return "FA_ERR_ARG: softmax_scale must be finite and > 0, num_splits >= 0, "
+                   "dropout_p in [0, 1)";
         case FA_ERR_TOO_LARGE:
             return "FA_ERR_TOO_LARGE: one (batch, head) slice exceeds 2 GiB";
         default: return "unknown fa status";
@@ -263,5 +280,30 @@ int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o, const
     return bwd_impl(true, q, k, v, o, lse, dout, dq, dk, dv, workspace, ws_bytes, B, H, N,
                     D, softmax_scale, causal, stream);
 }
+
+#define FA_DROPOUT_ENTRIES(SUFFIX, F16)                                                   \
+    int fa_fwd_dropout##SUFFIX(const void* q, const void* k, const void* v, void* o,      \
+                               float* lse, int B, int H, int N, int D,                    \
+                               float softmax_scale, int causal, float dropout_p,          \
+                               uint64_t seed, uint64_t offset, hipStream_t stream) {      \
+        fa::Dropout d{};                                                                   \
+        if (int rc = make_dropout(dropout_p, seed, offset, d)) return rc;                  \
+        return fwd_impl(F16, q, k, v, o, lse, B, H, N, D, softmax_scale, causal, stream,  \
+                        &d);                                                               \
+    }                                                                                      \
+    int fa_bwd_dropout##SUFFIX(const void* q, const void* k, const void* v, const void* o, \
+                               const float* lse, const void* dout, void* dq, void* dk,    \
+                               void* dv, void* workspace, size_t ws_bytes, int B, int H,  \
+                               int N, int D, float softmax_scale, int causal,             \
+                               float dropout_p, uint64_t seed, uint64_t offset,           \
+                               hipStream_t stream) {                                       \
+        fa::Dropout d{};                                                                   \
+        if (int rc = make_dropout(dropout_p, seed, offset, d)) return rc;                  \
+        return bwd_impl(F16, q, k, v, o, lse, dout, dq, dk, dv, workspace, ws_bytes, B, H,  \
+                        N, D, softmax_scale, causal, stream, &d);                          \
+    }
+FA_DROPOUT_ENTRIES(, false)
+FA_DROPOUT_ENTRIES(_f16, true)
+#undef FA_DROPOUT_ENTRIES
 
 }  // extern "C"

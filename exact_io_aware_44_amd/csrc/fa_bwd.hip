@@ -55,6 +55,7 @@ struct BwdParams {
     int per_head;  // dK/dV units per (batch, head): key tiles, or pairs if causal
     float c;       // scale * log2(e)
     float scale;
+    Dropout drop;  // the forward's drop decisions, replayed
 };
 
 // Direct global -> LDS load of one dword per lane (lane i writes M0 + 4*i).
@@ -156,7 +157,7 @@ __device__ __forceinline__ void mfma_acc_drain(f32x16& a, f32x16& b) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a), "+a"(b));
 }
 
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     using T = KvTile<D>;
     // one LDS object per buffer, selected statically, so the compiler can tell
@@ -252,13 +253,25 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
             const f32x4 nl = *reinterpret_cast<const f32x4*>(fs + 32 * b + 8 * a + 4 * hi);
             const f32x4 dd =
                 *reinterpret_cast<const f32x4*>(fs + T::BQ + 32 * b + 8 * a + 4 * hi);
+            // dropout: one generator call covers this lane's key and the 4
+            // queries of group a (word x: query +x; byte: key % 4)
+            u32x4 blk{};
+            if constexpr (DROP) blk = dropout_block(p.drop, head, qb0 + 8 * a + 4 * hi, kj);
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int r = 4 * a + x;
                 float pv = exp2_fast(__builtin_fmaf(s[r], p.c, nl[x]));
                 if (MASK) pv = tm > 8 * a + x ? 0.f : pv;
-                pf[r] = pv;
-                sf[r] = pv * (dp[r] - dd[x]);
+                if constexpr (DROP) {
+                    // dV takes the kept weights P Z, dS = P (dP Z - D)
+                    const float z = dropout_keep(blk[x], kj & 3, p.drop.thresh)
+                                        ? p.drop.inv_keep : 0.f;
+                    pf[r] = pv * z;
+                    sf[r] = pv * (dp[r] * z - dd[x]);
+                } else {
+                    pf[r] = pv;
+                    sf[r] = pv * (dp[r] - dd[x]);
+                }
             }
         }
         pb[0] = pack8<E>(pf);
@@ -402,8 +415,8 @@ struct QTile {
     static constexpr int DB = D / 32;
 };
 
-template <typename E, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
+template <typename E, int D, bool CAUSAL, bool DROP>
+__global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
     using T = QTile<D>;
     __shared__ __attribute__((aligned(16))) bf16 k_lds0[T::T_ELEMS];
     __shared__ __attribute__((aligned(16))) bf16 k_lds1[T::T_ELEMS];
@@ -483,11 +496,22 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int lim = qi - kb0 - 4 * hi;  // masked where local key offset > lim
         float sf[16];
+        u32x4 blk{};
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float pv = exp2_fast(__builtin_fmaf(s[r], p.c, nl2));
             if (MASK) pv = 8 * (r >> 2) + (r & 3) > lim ? 0.f : pv;
-            sf[r] = pv * (dp[r] - dd);
+            if constexpr (DROP) {
+                // one generator call per group of 4 keys; this lane reads the
+                // word of its query
+                if ((r & 3) == 0) blk = dropout_block(p.drop, head, qi, kb0 + 8 * (r >> 2) + 4 * hi);
+                const int w = qi & 3;
+                const uint32_t word = w == 0 ? blk[0] : w == 1 ? blk[1] : w == 2 ? blk[2] : blk[3];
+                const float z = dropout_keep(word, r & 3, p.drop.thresh) ? p.drop.inv_keep : 0.f;
+                sf[r] = pv * (dp[r] * z - dd);
+            } else {
+                sf[r] = pv * (dp[r] - dd);
+            }
         }
         sb[0] = pack8<E>(sf);
         sb[1] = pack8<E>(sf + 8);
@@ -599,7 +623,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     }
 }
 
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL, bool DROP>
 hipError_t run_bwd(const BwdArgs& a, hipStream_t stream) {
     BwdParams p;
     p.q = static_cast<const bf16*>(a.q);
@@ -618,6 +642,7 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream) {
     p.N = a.N;
     p.c = (float)((double)a.scale * 1.4426950408889634);
     p.scale = a.scale;
+    p.drop = a.drop;
 
     const int64_t threads = rows * (D / 8);
     hipLaunchKernelGGL((dsum_kernel<E, D>), dim3((unsigned)((threads + 255) / 256)),
@@ -628,7 +653,7 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream) {
     const int nkt = (a.N + KvTile<D>::BK - 1) / KvTile<D>::BK;
     p.per_head = CAUSAL ? (nkt + 1) / 2 : nkt;
     const int64_t units = (int64_t)p.per_head * a.H * a.B;
-    hipLaunchKernelGGL((dkdv_kernel<E, D, CAUSAL>), dim3((unsigned)units), dim3(256), 0,
+    hipLaunchKernelGGL((dkdv_kernel<E, D, CAUSAL, DROP>), dim3((unsigned)units), dim3(256), 0,
                        stream, p);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -637,16 +662,22 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream) {
     const int nqt = (a.N + QTile<D>::BR - 1) / QTile<D>::BR;
     p.per_head = CAUSAL ? (nqt + 1) / 2 : nqt;
     const int64_t qunits = (int64_t)p.per_head * a.H * a.B;
-    hipLaunchKernelGGL((dq_kernel<E, D, CAUSAL>), dim3((unsigned)qunits), dim3(256), 0, stream,
+    hipLaunchKernelGGL((dq_kernel<E, D, CAUSAL, DROP>), dim3((unsigned)qunits), dim3(256), 0, stream,
                        p);
     return hipGetLastError();
 }
 
+template <typename E, bool DROP>
+hipError_t run_bwd_d(const BwdArgs& a, hipStream_t stream) {
+    if (a.D == 64)
+        return a.causal ? run_bwd<E, 64, true, DROP>(a, stream)
+                        : run_bwd<E, 64, false, DROP>(a, stream);
+    return a.causal ? run_bwd<E, 128, true, DROP>(a, stream)
+                    : run_bwd<E, 128, false, DROP>(a, stream);
+}
 template <typename E>
 hipError_t run_bwd_e(const BwdArgs& a, hipStream_t stream) {
-    if (a.D == 64)
-        return a.causal ? run_bwd<E, 64, true>(a, stream) : run_bwd<E, 64, false>(a, stream);
-    return a.causal ? run_bwd<E, 128, true>(a, stream) : run_bwd<E, 128, false>(a, stream);
+    return a.drop.thresh > 0 ? run_bwd_d<E, true>(a, stream) : run_bwd_d<E, false>(a, stream);
 }
 
 }  // namespace

@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_launch.hpp"  // Dropout
+
 namespace fa {
 
 // 16-bit elements travel (global, LDS, registers) as bf16-typed vectors; the
@@ -186,6 +188,45 @@ __device__ __forceinline__ float pair_sum(float x) {
 template <typename E>
 __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
     return u32x2{pack2<E>(a, b), pack2<E>(c, d)};
+}
+
+// ---- attention dropout -------------------------------------------------------
+// Drop decisions come from the counter-based generator Philox4x32-10 (Salmon,
+// Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC
+// 2011): ten rounds, each forming the 64-bit products 0xD2511F53 * c0 and
+// 0xCD9E8D57 * c2 and mixing their halves with c1, c3 and the key, the key
+// advancing by (0x9E3779B9, 0xBB67AE85) between rounds.  For query i and key
+// j of head bh the counter is (j / 4, i / 4, bh, offset) and the key the
+// 64-bit seed; byte j % 4 of output word i % 4 is compared with the threshold
+// T (kept iff >= T), so one call decides a 4 x 4 block of (query, key) pairs.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                               uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+    }
+    return u32x4{c0, c1, c2, c3};
+}
+
+// The decision bytes of the 4 x 4 block holding (query i, key j): word w of
+// the result holds queries i0 + w (i0 = i & ~3), byte t keys j0 + t.
+__device__ __forceinline__ u32x4 dropout_block(const Dropout& d, uint32_t bh, int i, int j) {
+    return philox4x32_10((uint32_t)j >> 2, (uint32_t)i >> 2, bh, d.offset, d.seed_lo,
+                         d.seed_hi);
+}
+__device__ __forceinline__ bool dropout_keep(uint32_t word, int byte, uint32_t thresh) {
+    return ((word >> (8 * byte)) & 0xFFu) >= thresh;
 }
 
 }  // namespace fa

@@ -108,6 +108,7 @@ struct FwdParams {
     int heads;     // B * H
     float* part_o;
     float* part_l;
+    Dropout drop;  // attention dropout (dense forward only)
 };
 
 // Unit schedule.  Workgroup i of a 1-D grid is dispatched to XCD i % 8; the
@@ -123,7 +124,7 @@ __device__ __forceinline__ void unit_of(int i, int total, int per_head, int& hea
 using True = std::true_type;
 using False = std::false_type;
 
-template <typename E, int D, bool CAUSAL, bool VARLEN, bool SPLIT>
+template <typename E, int D, bool CAUSAL, bool VARLEN, bool SPLIT, bool DROP>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     using T = FwdTile<D>;
     // Separate LDS objects per buffer, always selected statically, so the
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 
     // online softmax of one half: new running maximum (lazy), rescale factor,
     // exponentials as bf16 B operands, row sum
-    auto softmax = [&](f32x16& s, bf16x8 (&pb)[2], float& alpha, bool& upd) {
+    auto softmax = [&](f32x16& s, bf16x8 (&pb)[2], float& alpha, bool& upd, int hsm) {
         float t4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -295,6 +296,20 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         for (int r = 0; r < 16; ++r) {
             s[r] = exp2_fast(__builtin_fmaf(s[r], p.c, -m_use));
             rs[r & 3] = r < 4 ? s[r] : rs[r & 3] + s[r];
+        }
+        if constexpr (DROP) {
+            // dropped weights leave the P.V operand, not the sum l (L is the
+            // log-sum-exp of all allowed scores); each group of 4 keys is one
+            // generator call, this lane reading the word of its query
+            const int w = qi & 3;
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const u32x4 blk = dropout_block(p.drop, head, qi, 32 * hsm + 8 * a + 4 * hi);
+                const uint32_t word = w == 0 ? blk[0] : w == 1 ? blk[1] : w == 2 ? blk[2] : blk[3];
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    if (!dropout_keep(word, x, p.drop.thresh)) s[4 * a + x] = 0.f;
+            }
         }
         pb[0] = pack8<E>(s, 0);
         pb[1] = pack8<E>(s, 8);
@@ -333,7 +348,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     //      MFMAs alternate S / P.V (independent neighbours) and every operand
     //      is requested from LDS four MFMAs ahead; the compiler interleaves
     //      the softmax VALU work (pinning a fixed pattern measured slower). --
-    auto half_step = [&](auto do_s, auto do_pv, auto do_sm, const bf16* ks, int kh,
+    auto half_step = [&](auto do_s, auto do_pv, auto do_sm, int hsm, const bf16* ks, int kh,
                          const bf16* vs, int vh, f32x16& s_cur, f32x16& s_nxt,
                          const bf16x8 (&pb_prev)[2], bf16x8 (&pb_new)[2], float& alpha,
                          bool& upd) {
@@ -361,7 +376,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         bf16x8 op[NM > 0 ? NM : 1];
 #pragma unroll
         for (int i = 0; i < PF && i < NM; ++i) op[i] = fetch(i);
-        if constexpr (DO_SM) softmax(s_cur, pb_new, alpha, upd);
+        if constexpr (DO_SM) softmax(s_cur, pb_new, alpha, upd, hsm);
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
             if (i + PF < NM) op[i + PF] = fetch(i + PF);
@@ -387,7 +402,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     #pragma unroll
         for (int ss = 0; ss < T::DS; ++ss) sA = mfma32<E>(k_op(k_lds0, 0, ss), qreg[ss], sA);
         if (needs_mask(0)) apply_mask(sA, 0);
-        half_step(True{}, False{}, True{}, k_lds0, 1, nullptr, 0, sA, sB, pB, pA, alpha, upd);
+        half_step(True{}, False{}, True{}, 0, k_lds0, 1, nullptr, 0, sA, sB, pB, pA, alpha, upd);
         l_run = l_new;  // first half: nothing to rescale
         __syncthreads();  // K_0 is consumed before tile-step 0 reloads its buffer
 
@@ -405,10 +420,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
             if (j + 2 < nkt) load_k((j + 2) * T::BC, k_wr);
             load_v((j + 1) * T::BC, v_wr);
             if (needs_mask(2 * j + 1)) apply_mask(sB, 2 * j + 1);
-            half_step(True{}, True{}, True{}, k_rd, 0, v_rd, 0, sB, sA, pA, pB, alpha, upd);
+            half_step(True{}, True{}, True{}, 2 * j + 1, k_rd, 0, v_rd, 0, sB, sA, pA, pB, alpha,
+                      upd);
             rescale(alpha, upd);
             if (needs_mask(2 * j + 2)) apply_mask(sA, 2 * j + 2);
-            half_step(True{}, True{}, True{}, k_rd, 1, v_rd, 1, sA, sB, pB, pA, alpha, upd);
+            half_step(True{}, True{}, True{}, 2 * j + 2, k_rd, 1, v_rd, 1, sA, sB, pB, pA, alpha,
+                      upd);
             rescale(alpha, upd);
             wait_vmem();  // K_{j+2} and V_{j+1} landed
             barrier_only();
@@ -424,9 +441,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
             const int j = nkt - 1;
             const bf16* v_rd = (j & 1) ? v_lds1 : v_lds0;
             if (needs_mask(2 * j + 1)) apply_mask(sB, 2 * j + 1);
-            half_step(False{}, True{}, True{}, nullptr, 0, v_rd, 0, sB, sA, pA, pB, alpha, upd);
+            half_step(False{}, True{}, True{}, 2 * j + 1, nullptr, 0, v_rd, 0, sB, sA, pA, pB,
+                      alpha, upd);
             rescale(alpha, upd);
-            half_step(False{}, True{}, False{}, nullptr, 0, v_rd, 1, sA, sB, pB, pA, alpha, upd);
+            half_step(False{}, True{}, False{}, 0, nullptr, 0, v_rd, 1, sA, sB, pB, pA, alpha,
+                      upd);
         }
         __syncthreads();  // LDS reads done before the next tile of the unit reloads
     }
@@ -434,7 +453,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     // epilogue: O = u / l (bf16), L = m + ln l (natural log, scaled units);
     // in split mode the same quantities of the key range, in fp32
     const float l_tot = pair_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // kept weights carry 1 / (1 - p'), folded into the normalisation
+    const float inv = l_tot > 0.f ? (DROP ? p.drop.inv_keep : 1.f) / l_tot : 0.f;
     const float L = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : kNegInf;
 #pragma unroll
     for (int e = 0; e < T::DB; ++e)
@@ -486,7 +506,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* part_o, const f
     if (lse && c == 0) lse[row] = L;
 }
 
-template <typename E, int D, bool CAUSAL, bool VARLEN, bool SPLIT>
+template <typename E, int D, bool CAUSAL, bool VARLEN, bool SPLIT, bool DROP = false>
 hipError_t run_fwd(const FwdArgs& a, hipStream_t stream) {
     using T = FwdTile<D>;
     FwdParams p;
@@ -509,7 +529,8 @@ hipError_t run_fwd(const FwdArgs& a, hipStream_t stream) {
     p.part_o = a.part;
     p.part_l = a.part + ((rows * a.splits * D + 63) & ~(int64_t)63);
     const int64_t units = (int64_t)p.per_head * a.H * a.B;
-    hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, VARLEN, SPLIT>), dim3((unsigned)units),
+    p.drop = a.drop;
+    hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, VARLEN, SPLIT, DROP>), dim3((unsigned)units),
                        dim3(T::THREADS), 0, stream, p);
     if (!SPLIT) return hipGetLastError();
     hipError_t err = hipGetLastError();
@@ -523,6 +544,9 @@ hipError_t run_fwd(const FwdArgs& a, hipStream_t stream) {
 template <typename E, int D>
 hipError_t run_fwd_d(const FwdArgs& a, hipStream_t stream) {
     const bool varlen = a.cu != nullptr;
+    if (a.drop.thresh > 0)  // dropout: dense batch only
+        return a.causal ? run_fwd<E, D, true, false, false, true>(a, stream)
+                        : run_fwd<E, D, false, false, false, true>(a, stream);
     if (a.splits > 1)
         return a.causal ? run_fwd<E, D, true, false, true>(a, stream)
                         : run_fwd<E, D, false, false, true>(a, stream);

@@ -8,6 +8,14 @@
 
 namespace fa {
 
+// Attention dropout parameters: generator seed and offset, drop threshold T
+// (a decision byte below T drops the weight) and the scale of kept weights.
+struct Dropout {
+    uint32_t seed_lo, seed_hi, offset;
+    uint32_t thresh;   // T in [0, 255]; 0 = no dropout
+    float inv_keep;    // 256 / (256 - T)
+};
+
 struct FwdArgs {
     const void* q;
     const void* k;
@@ -27,6 +35,7 @@ struct FwdArgs {
     int chunk = 0;          // keys per split, a multiple of 64
     float* part = nullptr;  // split workspace: partial O, then partial L (fp32)
     bool f16 = false;       // element type: bf16, or fp16 when set
+    Dropout drop{};         // thresh 0: no dropout
 };
 
 struct BwdArgs {
@@ -45,6 +54,7 @@ struct BwdArgs {
     float scale;
     bool causal;
     bool f16 = false;       // element type: bf16, or fp16 when set
+    Dropout drop{};         // thresh 0: no dropout
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);

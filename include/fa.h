@@ -62,8 +62,8 @@ enum fa_status {
     FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
     FA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required         */
     FA_ERR_LAUNCH = 6,      /* a kernel launch failed (HIP error)              */
-    FA_ERR_ARG = 7,         /* softmax_scale not finite or not > 0, or a
-                               negative num_splits                             */
+    FA_ERR_ARG = 7,         /* softmax_scale not finite or not > 0, a negative
+                               num_splits, or dropout_p outside [0, 1)        */
     FA_ERR_TOO_LARGE = 8    /* a (batch, head) slice exceeds 2 GiB             */
 };
 
@@ -200,6 +200,39 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            float softmax_scale, int causal, hipStream_t stream);
 
 /*
+ * Attention dropout (tensortonic section 7: with dropout enabled the
+ * backward pass must reproduce the forward pass's drop decisions from saved
+ * generator state, never draw a new mask).  After the softmax each weight
+ * P_ij is kept with probability 1 - p' and scaled by 1 / (1 - p'), or set to
+ * zero; O uses the dropped weights while lse stays the log-sum-exp of all
+ * allowed scores.  The decisions are a pure function of (seed, offset, head,
+ * query, key): the counter-based generator Philox4x32-10 (Salmon et al.,
+ * SC 2011) with counter (key / 4, query / 4, b * H + h, offset mod 2^32) and
+ * key seed; byte key % 4 of output word query % 4 is compared with
+ * T = min(255, round(256 * dropout_p)) and the weight kept iff it is >= T,
+ * so p' = T / 256 (dropout_p is rounded to a multiple of 1/256).  Passing the
+ * same seed and offset to fa_bwd_dropout replays the forward's mask; no mask
+ * is stored.
+ *
+ *   dropout_p   in [0, 1); T = 0 (dropout_p < 1/512) is attention without
+ *               dropout.  Otherwise FA_ERR_ARG.
+ *   seed        64-bit generator key
+ *   offset      generator counter offset (low 32 bits used); advance it per
+ *               call to draw fresh masks under one seed
+ *
+ * Other arguments, layouts and status codes are those of fa_fwd and fa_bwd
+ * (dense batch only).
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int H, int N, int D, float softmax_scale, int causal, float dropout_p,
+                   uint64_t seed, uint64_t offset, hipStream_t stream);
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes, int B, int H, int N, int D,
+                   float softmax_scale, int causal, float dropout_p, uint64_t seed,
+                   uint64_t offset, hipStream_t stream);
+
+/*
  * FP16 variants (nexusofnerds "What is FlashAttention?": the kernels run in
  * mixed precision with BF16 or FP16 inputs).  Each has the contract of the
  * function without the suffix, with every 16-bit tensor (q, k, v, o, dout,
@@ -224,6 +257,14 @@ int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o, const
                const void* dout, void* dq, void* dk, void* dv, void* workspace,
                size_t workspace_bytes, int B, int H, int N, int D, float softmax_scale,
                int causal, hipStream_t stream);
+int fa_fwd_dropout_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int N, int D, float softmax_scale, int causal,
+                       float dropout_p, uint64_t seed, uint64_t offset, hipStream_t stream);
+int fa_bwd_dropout_f16(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, int B, int H, int N, int D,
+                       float softmax_scale, int causal, float dropout_p, uint64_t seed,
+                       uint64_t offset, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_string(int status);

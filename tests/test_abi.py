@@ -35,8 +35,10 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert names == ["fa_bwd", "fa_bwd_f16", "fa_bwd_workspace_size", "fa_fwd",
-                     "fa_fwd_f16", "fa_fwd_qk", "fa_fwd_qk_f16", "fa_fwd_splitkv",
+    assert names == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_dropout_f16", "fa_bwd_f16",
+                     "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_dropout",
+                     "fa_fwd_dropout_f16", "fa_fwd_f16", "fa_fwd_qk", "fa_fwd_qk_f16",
+                     "fa_fwd_splitkv",
                      "fa_fwd_splitkv_f16", "fa_fwd_splitkv_workspace_size",
                      "fa_fwd_varlen", "fa_fwd_varlen_f16", "fa_status_string"]
     for n in names:
@@ -119,6 +121,22 @@ def test_splitkv_workspace_size():
     assert ws(1, 1, 1, 100, 64, 50) == 4 * (2 * 64 + 64)  # at most one range per 64 keys
     assert ws(0, 4, 1, 4096, 128) == 0 and ws(2, 4, 1, 4096, 96) == 0
     assert ws(2, 4, 1, 4096, 128, -1) == 0
+
+
+@pytest.mark.parametrize("f16", [False, True])
+@pytest.mark.parametrize("pdrop,code", [(-0.1, ARG), (1.0, ARG), (1.5, ARG),
+                                        (float("nan"), ARG), (float("inf"), ARG)])
+def test_dropout_rejects(lib, pdrop, code, f16):
+    sfx = "_f16" if f16 else ""
+    fwd_d = getattr(lib, "fa_fwd_dropout" + sfx)
+    bwd_d = getattr(lib, "fa_bwd_dropout" + sfx)
+    assert fwd_d(P, P, P, P, P, 1, 2, 64, 128, 0.1, 1, pdrop, 1, 0, None) == code
+    assert bwd_d(P, P, P, P, P, P, P, P, P, P, 1 << 30, 1, 2, 64, 128, 0.1, 1, pdrop, 1, 0,
+                 None) == code
+    # a valid probability with one other invalid argument reports that one
+    assert fwd_d(P, P, P, P, P, 1, 2, 64, 96, 0.1, 1, 0.2, 1, 0, None) == UNSUP
+    assert bwd_d(P, P, P, P, P, P, P, P, P, None, 1 << 30, 1, 2, 64, 128, 0.1, 1, 0.2, 1, 0,
+                 None) == WS
 
 
 def varlen(lib, q=P, k=P, v=P, o=P, lse=P, cu=P, nseq=2, total=32, maxlen=16,
