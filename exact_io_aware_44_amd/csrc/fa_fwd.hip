@@ -382,6 +382,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
             if (i + PF < NM) op[i + PF] = fetch(i + PF);
             apply(i, op[i]);
         }
+        // the new weights and their sum are due here, inside this block of
+        // MFMAs, not after the rescale branch that follows the half-step:
+        // otherwise the compiler sinks the exponentials past that branch,
+        // into a block with no matrix work to overlap
+        if constexpr (DO_SM) {
+            const bf16x8 w0 = pb_new[0], w1 = pb_new[1];
+            const float ls = l_new;
+            asm volatile("" ::"v"(w0), "v"(w1), "v"(ls));
+        }
     };
 
     // a tile whose queries all precede the first key reads nothing: O = 0,
@@ -415,25 +424,42 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         // The buffer pointers are __restrict__: the tile a DMA is filling never
         // overlaps a tile being read, which lets the compiler leave the loads in
         // flight while the reads proceed.
+        // MASKED: the tile-step may hold halves on the causal diagonal or past
+        // the end; interior tile-steps skip the checks, so their body holds
+        // no branch besides the (rare) rescale
         auto tile_step = [&](int j, const bf16* __restrict__ k_rd, const bf16* __restrict__ v_rd,
-                             bf16* __restrict__ k_wr, bf16* __restrict__ v_wr) {
+                             bf16* __restrict__ k_wr, bf16* __restrict__ v_wr, auto mask_tag) {
+            constexpr bool MASKED = decltype(mask_tag)::value;
             if (j + 2 < nkt) load_k((j + 2) * T::BC, k_wr);
             load_v((j + 1) * T::BC, v_wr);
-            if (needs_mask(2 * j + 1)) apply_mask(sB, 2 * j + 1);
+            if (MASKED && needs_mask(2 * j + 1)) apply_mask(sB, 2 * j + 1);
             half_step(True{}, True{}, True{}, 2 * j + 1, k_rd, 0, v_rd, 0, sB, sA, pA, pB, alpha,
                       upd);
             rescale(alpha, upd);
-            if (needs_mask(2 * j + 2)) apply_mask(sA, 2 * j + 2);
+            if (MASKED && needs_mask(2 * j + 2)) apply_mask(sA, 2 * j + 2);
             half_step(True{}, True{}, True{}, 2 * j + 2, k_rd, 1, v_rd, 1, sA, sB, pB, pA, alpha,
                       upd);
             rescale(alpha, upd);
             wait_vmem();  // K_{j+2} and V_{j+1} landed
             barrier_only();
         };
-        for (int j = 0; j + 1 < nkt; ++j) {
+        // tile-steps whose halves 2j+1, 2j+2 all lie before the diagonal and
+        // the end need no mask: j < j_int
+        // (half 2j+2 ends at key 64j + 95: it must not pass the first row's
+        // limit q0 + shift, nor the last key nk - 1)
+        int j_int = (nk - 32) / T::BC;
+        if (CAUSAL) j_int = min(j_int, (q0 + shift - 31) / T::BC);
+        j_int = max(0, min(j_int, nkt - 1));
+        int j = 0;
+        for (; j < j_int; ++j) {
             const bool odd = j & 1;
             tile_step(j, odd ? k_lds0 : k_lds1, odd ? v_lds1 : v_lds0, odd ? k_lds1 : k_lds0,
-                      odd ? v_lds0 : v_lds1);
+                      odd ? v_lds0 : v_lds1, False{});
+        }
+        for (; j + 1 < nkt; ++j) {
+            const bool odd = j & 1;
+            tile_step(j, odd ? k_lds0 : k_lds1, odd ? v_lds1 : v_lds0, odd ? k_lds1 : k_lds0,
+                      odd ? v_lds0 : v_lds1, True{});
         }
         // last tile-step j = nkt - 1: softmax of half 2nkt-1 with P.V of half
         // 2nkt-2, then P.V of half 2nkt-1
