@@ -329,6 +329,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         l_run += l_new;
     };
 
+    uint32_t voffb[T::DB];
+#pragma unroll
+    for (int e = 0; e < T::DB; ++e) {
+        const int kr = 4 * hi + (i16 >> 2);
+        const int dcol = 32 * e + 16 * (g & 1) + 4 * (i16 & 3);
+        voffb[e] = (uint32_t)(kr * D + (((dcol >> 3) ^ v_swz<D>(kr)) << 3) + (dcol & 7)) * 2;
+    }
     // MFMA operands.  S: A = K rows (ds_read_b128), B = Q registers.  P.V:
     // A = V^T by transpose reads, B = P^T; rows kr, kr+8 (kr = 16bt + 4hi +
     // i16/4) share v_swz(kr), so the swizzled column depends on lane and e.
@@ -336,10 +343,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         return lds_read16(ks + (32 * half + l32) * T::KSTR + 16 * ss + 8 * hi);
     };
     auto v_op = [&](const bf16* vs, int bt, int e) {
-        const int kr = 16 * bt + 4 * hi + (i16 >> 2);
-        const int dcol = 32 * e + 16 * (g & 1) + 4 * (i16 & 3);
-        const int col = (((dcol >> 3) ^ v_swz<D>(kr)) << 3) + (dcol & 7);
-        return cat(lds_read_tr(vs + kr * D + col), lds_read_tr(vs + (kr + 8) * D + col));
+        // byte offset of this lane's read: row 4hi + i16/4 (+16 bt, +8),
+        // swizzled column of block e (the swizzle depends on the row mod 4
+        // only, so bt does not change it)
+        const char* p = reinterpret_cast<const char*>(vs) + voffb[e] + 16 * bt * D * 2;
+        return cat(lds_read_tr(reinterpret_cast<const bf16*>(p)),
+                   lds_read_tr(reinterpret_cast<const bf16*>(p + 8 * D * 2)));
     };
 
     // ---- one half-step: S of the next half (DS MFMAs, rows 32*kh of ks) if
@@ -451,6 +460,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         if (CAUSAL) j_int = min(j_int, (q0 + shift - 31) / T::BC);
         j_int = max(0, min(j_int, nkt - 1));
         int j = 0;
+        // two tile-steps per trip: the buffers of each are then static
+        for (; j + 1 < j_int; j += 2) {
+            tile_step(j, k_lds1, v_lds0, k_lds0, v_lds1, False{});
+            tile_step(j + 1, k_lds0, v_lds1, k_lds1, v_lds0, False{});
+        }
         for (; j < j_int; ++j) {
             const bool odd = j & 1;
             tile_step(j, odd ? k_lds0 : k_lds1, odd ? v_lds1 : v_lds0, odd ? k_lds1 : k_lds0,
