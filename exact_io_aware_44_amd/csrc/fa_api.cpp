@@ -50,9 +50,14 @@ size_t workspace_bytes(int B, int H, int N) {
     return 2 * ((rows * sizeof(float) + 255) & ~(size_t)255);
 }
 
+// Up to this many queries per (batch, head), fa_fwd_splitkv runs the decoding
+// kernel (all queries of a head in one wave's lanes).
+constexpr int kDecodeMaxQ = 32;
+
 // Key-range splits for fa_fwd_splitkv: the requested count (0 = automatic:
-// enough units for about 512 workgroups, two per CU, each range at least 256
-// keys; more ranges only add merge traffic and shorter streams),
+// for the decoding kernel about 256 workgroups, one per CU, each range at
+// least 512 keys; otherwise about 512 workgroups, two per CU, each range at
+// least 256 keys; more ranges only add merge traffic and shorter streams),
 // clamped to one 64-key tile per range, then rounded so every range but the
 // last holds a whole number of tiles and none is empty.
 struct Splits {
@@ -62,7 +67,12 @@ struct Splits {
 Splits pick_splits(int B, int H, int Nq, int Nk, int requested) {
     const int64_t units = (int64_t)B * H * ((Nq + 127) / 128);
     int64_t s = requested;
-    if (s == 0) {
+    if (s == 0 && Nq <= kDecodeMaxQ) {
+        // decoding kernel: one workgroup per CU (256 of them), each range at
+        // least 512 keys so every wave streams several blocks
+        s = std::min<int64_t>(128, (256 + units - 1) / units);
+        s = std::min<int64_t>(s, std::max(1, (Nk + 511) / 512));
+    } else if (s == 0) {
         s = std::min<int64_t>(128, (512 + units - 1) / units);
         s = std::min<int64_t>(s, std::max(1, (Nk + 255) / 256));
     }
@@ -136,6 +146,7 @@ int fwd_splitkv_impl(bool f16, const void* q, const void* k, const void* v, void
         a.part = static_cast<float*>(workspace);
     }
     a.f16 = f16;
+    a.decode = Nq <= kDecodeMaxQ;
     return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

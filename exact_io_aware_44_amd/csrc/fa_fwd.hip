@@ -546,6 +546,289 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* part_o, const f
     if (lse && c == 0) lse[row] = L;
 }
 
+// ---- decoding: a handful of queries against a long key range ---------------
+//
+// With N_q <= 32 every (batch, head) has one query tile, so the forward tile
+// of 128 rows would spend its matrix work on empty rows while the HBM stream
+// of K and V is what bounds the call.  This kernel is shaped for that stream:
+//  - the four waves of a workgroup take interleaved 32-key blocks of the
+//    unit's key range (wave w: blocks w, w + 4, ...) and run independently,
+//    with no barrier until the end;
+//  - K and V blocks are read with ordinary wave-wide loads of 1 KiB of
+//    consecutive rows into registers, two blocks ahead, so each CU keeps
+//    128 KiB in flight.  (Loading the MFMA operands themselves touches 32
+//    rows per load, 32 bytes each, and streams at about half the rate; the
+//    global->LDS DMA path tops out near 6.1 TB/s on this chip, plain loads
+//    near 7.)  A block is then written into the wave's own LDS region,
+//    K rows padded and V rows swizzled as in fwd_kernel, and read back as
+//    MFMA operands;
+//  - at the end the waves' (m, l, u) are merged through LDS by the same
+//    running-softmax rule, then O and L (or the range's partials) are stored.
+template <int D>
+struct DecTile {
+    static constexpr int BK = 32;                 // keys per block
+    static constexpr int CPR = D / 8;             // 16-byte chunks per row
+    static constexpr int RPL = 64 / CPR;          // V rows per wave-wide load
+    static constexpr int V_ELEMS = BK * D;        // one V block in LDS
+    static constexpr int KSTR = D + 8;            // padded K row (see FwdTile)
+    static constexpr int K_ELEMS = BK * KSTR;
+    static constexpr int LOADS = BK * CPR / 64;   // wave-wide 1 KiB loads per K or V block
+    static constexpr int DS = D / 16, DB = D / 32;
+};
+
+template <typename E, int D, bool CAUSAL, bool PART>
+__global__ __launch_bounds__(256, 1) void decode_kernel(FwdParams p) {
+    using T = DecTile<D>;
+    // each wave's current K and V block
+    __shared__ __attribute__((aligned(16))) bf16 k_st[4 * T::K_ELEMS];
+    __shared__ __attribute__((aligned(16))) bf16 v_st[4 * T::V_ELEMS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int g = lane >> 4, i16 = lane & 15;
+    int head, split;
+    unit_of(blockIdx.x, gridDim.x, p.splits, head, split);
+    const int b = head / p.H, h = head - b * p.H;
+
+    const int n = p.N;
+    int nk = p.Nk;
+    const int64_t row0 = ((int64_t)b * p.H + h) * n;
+    const int64_t krow0 = ((int64_t)b * p.H + h) * p.Nk;
+    int shift = nk - n;  // query i reads keys j <= i + shift (causal)
+    const int kbeg = min(nk, split * p.chunk);
+    nk = min(nk - kbeg, p.chunk);
+    shift -= kbeg;
+    // keys any query of the unit reads
+    const int kend = CAUSAL ? max(0, min(nk, n + shift)) : nk;
+    const int nblk = (kend + T::BK - 1) / T::BK;
+    // this wave's blocks: wave, wave + 4, ...
+    const int nb = nblk > wave ? (nblk - wave + 3) / 4 : 0;
+
+    const uint32_t kbytes = (uint32_t)nk * D * 2;
+    const Buf qb = make_buf(p.q + row0 * D, (uint32_t)n * D * 2);
+    const Buf kb = make_buf(p.k + (krow0 + kbeg) * D, kbytes);
+    const Buf vb = make_buf(p.v + (krow0 + kbeg) * D, kbytes);
+
+    const int qi = l32;  // query held by this lane (rows >= n read zeros)
+    bf16x8 qreg[T::DS];
+#pragma unroll
+    for (int s = 0; s < T::DS; ++s)
+        qreg[s] = __builtin_bit_cast(bf16x8,
+                                     load16(qb, ((uint32_t)qi * D + 16 * s + 8 * hi) * 2));
+
+    // load t of a block brings rows RPL t + lane / CPR, chunk lane % CPR; the
+    // lane stores its chunk at these LDS element offsets (row swizzle
+    // depends on lane only, as RPL is a multiple of 4)
+    const int lrow = lane / T::CPR, lch = lane % T::CPR;
+    const uint32_t gofs = (uint32_t)(lrow * D + lch * 8) * 2;
+    const int kls = lrow * T::KSTR + lch * 8;
+    const int vls = lrow * D + ((lch ^ v_swz<D>(lrow)) * 8);
+    static_assert(T::RPL % 4 == 0, "swizzle of row RPL t + r equals that of r");
+    uint32_t voffb[T::DB];
+#pragma unroll
+    for (int e = 0; e < T::DB; ++e) {
+        const int kr = 4 * hi + (i16 >> 2);
+        const int dcol = 32 * e + 16 * (g & 1) + 4 * (i16 & 3);
+        voffb[e] = (uint32_t)(kr * D + (((dcol >> 3) ^ v_swz<D>(kr)) << 3) + (dcol & 7)) * 2;
+    }
+    bf16* const kw = k_st + wave * T::K_ELEMS;
+    bf16* const vw = v_st + wave * T::V_ELEMS;
+
+    // block i of this wave: keys 32 * (wave + 4 i) .. of the range (rows
+    // past the range read zeros).  Requests for blocks past the wave's last
+    // are still issued, out of range (no memory access), so every step has
+    // the same number of loads in flight and the compiler's waits stay exact.
+    struct Blk {
+        u32x4 k[T::LOADS], v[T::LOADS];
+    };
+    auto issue = [&](int i, Blk& r) {
+        const uint32_t o = i < nb ? (uint32_t)(wave + 4 * i) * T::BK * D * 2 + gofs : kOutOfRange;
+#pragma unroll
+        for (int t = 0; t < T::LOADS; ++t) r.k[t] = load16(kb, o + t * 1024);
+#pragma unroll
+        for (int t = 0; t < T::LOADS; ++t) r.v[t] = load16(vb, o + t * 1024);
+    };
+    // LDS reads of the previous block come first in the wave's LDS queue,
+    // so the writes can follow them directly
+    auto stage = [&](const Blk& r) {
+#pragma unroll
+        for (int t = 0; t < T::LOADS; ++t) {
+            lds_write16(kw + kls + T::RPL * t * T::KSTR, r.k[t]);
+            lds_write16(vw + vls + T::RPL * t * D, r.v[t]);
+        }
+    };
+
+    f32x16 acc[T::DB];
+#pragma unroll
+    for (int e = 0; e < T::DB; ++e) acc[e] = f32x16{};
+    float m_run = kNegInf, l_run = 0.f;
+
+    auto block = [&](int i, const bf16* ks, const bf16* vs) {
+        const int blk = wave + 4 * i;
+        f32x16 s = f32x16{};
+#pragma unroll
+        for (int ss = 0; ss < T::DS; ++ss)
+            s = mfma32<E>(lds_read16(ks + l32 * T::KSTR + 16 * ss + 8 * hi), qreg[ss], s);
+        // mask keys past the range end or after the query's causal limit
+        int lim = nk - T::BK * blk;
+        if (CAUSAL) lim = min(lim, qi + shift - T::BK * blk + 1);
+        if (lim < T::BK) {
+            lim -= 4 * hi;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (8 * (r / 4) + (r & 3) >= lim) s[r] = kNegInf;
+        }
+        float mx = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = pair_max(mx) * p.c;
+        const bool upd = mx > m_run + kLazyRescale;
+        const float m_new = upd ? mx : m_run;
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = m_run - m_use;
+        m_run = m_new;
+        float rs[4];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            s[r] = exp2_fast(__builtin_fmaf(s[r], p.c, -m_use));
+            rs[r & 3] = r < 4 ? s[r] : rs[r & 3] + s[r];
+        }
+        const bf16x8 pb0 = pack8<E>(s, 0), pb1 = pack8<E>(s, 8);
+        if (__any(upd)) {
+            const float f = exp2_fast(alpha);
+#pragma unroll
+            for (int e = 0; e < T::DB; ++e) acc[e] *= f;
+            l_run *= f;
+        }
+        l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+#pragma unroll
+        for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+            for (int e = 0; e < T::DB; ++e) {
+                const char* vp = reinterpret_cast<const char*>(vs) + voffb[e] + 16 * bt * D * 2;
+                const bf16x8 a = cat(lds_read_tr(reinterpret_cast<const bf16*>(vp)),
+                                     lds_read_tr(reinterpret_cast<const bf16*>(vp + 8 * D * 2)));
+                acc[e] = mfma32<E>(a, bt ? pb1 : pb0, acc[e]);
+            }
+    };
+
+    // each step: block i's registers (loaded two steps before) go to LDS,
+    // block i + 2 is requested into the same registers, block i is computed;
+    // two steps per trip keep the register sets static
+    Blk r0, r1;
+    issue(0, r0);
+    issue(1, r1);
+    auto step = [&](int i, Blk& r) {
+        stage(r);  // waits for block i's loads only
+        issue(i + 2, r);
+        block(i, kw, vw);
+    };
+    int i = 0;
+    for (; i + 1 < nb; i += 2) {
+        step(i, r0);
+        step(i + 1, r1);
+    }
+    if (i < nb) step(i, r0);
+
+    // ---- merge the four waves: stage (m, l, u) in LDS and let each thread
+    //      combine some (query, 4 columns) items; u goes in two passes of half
+    //      the columns, each filling one stage object --------------------------
+    __syncthreads();  // every wave is done with its blocks
+    constexpr int HD = D / 2;                             // columns per pass
+    float* const cu_o = reinterpret_cast<float*>(v_st);   // [4][32][HD]
+    float* const cm = reinterpret_cast<float*>(k_st);     // [4][32]
+    float* const cl = cm + 4 * 32;                        // [4][32]
+    static_assert(4 * 32 * HD * 4 <= 4 * T::V_ELEMS * 2, "half of u fits the V blocks");
+    const float l_tot = pair_sum(l_run);
+    if (hi == 0) {
+        cm[wave * 32 + qi] = m_run;
+        cl[wave * 32 + qi] = l_tot;
+    }
+    constexpr int TPR = HD / 4;  // items per query row and pass
+    const int64_t prow0 = ((int64_t)split * p.heads + head) * n;
+    const int nq = min(n, 32);
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int e = pass * T::DB / 2; e < (pass + 1) * T::DB / 2; ++e)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = 32 * e + 8 * r4 + 4 * hi - pass * HD;
+                *reinterpret_cast<f32x4*>(cu_o + (wave * 32 + qi) * HD + d) =
+                    f32x4{acc[e][4 * r4], acc[e][4 * r4 + 1], acc[e][4 * r4 + 2],
+                          acc[e][4 * r4 + 3]};
+            }
+        __syncthreads();
+        for (int it = tid; it < nq * TPR; it += 256) {
+            const int q = it / TPR, c = it - q * TPR;
+            float M = kNegInf;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) M = fmaxf(M, cm[w * 32 + q]);
+            f32x4 o{0.f, 0.f, 0.f, 0.f};
+            float lsum = 0.f;
+            if (M != kNegInf) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float f = exp2_fast(cm[w * 32 + q] - M);  // 0 for an empty wave
+                    lsum += f * cl[w * 32 + q];
+                    o += f * *reinterpret_cast<const f32x4*>(cu_o + (w * 32 + q) * HD + 4 * c);
+                }
+            }
+            const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+            o *= inv;
+            const int col = pass * HD + 4 * c;
+            if constexpr (PART) {
+                *reinterpret_cast<f32x4*>(p.part_o + (prow0 + q) * D + col) = o;
+            } else {
+                *reinterpret_cast<u32x2*>(p.o + (row0 + q) * D + col) =
+                    pack4<E>(o[0], o[1], o[2], o[3]);
+            }
+            if (pass == 0 && c == 0) {
+                const float L = lsum > 0.f ? (M + log2_fast(lsum)) * kLn2 : kNegInf;
+                if constexpr (PART) p.part_l[prow0 + q] = L;
+                else if (p.lse) p.lse[row0 + q] = L;
+            }
+        }
+        __syncthreads();  // the next pass overwrites the staged columns
+    }
+}
+
+template <typename E, int D, bool CAUSAL>
+hipError_t run_decode(const FwdArgs& a, hipStream_t stream) {
+    FwdParams p{};
+    p.q = static_cast<const bf16*>(a.q);
+    p.k = static_cast<const bf16*>(a.k);
+    p.v = static_cast<const bf16*>(a.v);
+    p.o = static_cast<bf16*>(a.o);
+    p.lse = a.lse;
+    p.H = a.H;
+    p.N = a.N;
+    p.Nk = a.Nk;
+    p.c = (float)((double)a.scale * 1.4426950408889634);
+    p.splits = a.splits;
+    p.chunk = a.splits > 1 ? a.chunk : a.Nk;
+    p.heads = a.B * a.H;
+    const int64_t rows = (int64_t)a.B * a.H * a.N;
+    p.part_o = a.part;
+    p.part_l = a.part ? a.part + ((rows * a.splits * D + 63) & ~(int64_t)63) : nullptr;
+    const unsigned units = (unsigned)((int64_t)a.B * a.H * a.splits);
+    if (a.splits > 1) {
+        hipLaunchKernelGGL((decode_kernel<E, D, CAUSAL, true>), dim3(units), dim3(256), 0,
+                           stream, p);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        const int64_t threads = rows * (D / 4);
+        hipLaunchKernelGGL((merge_kernel<E, D>), dim3((unsigned)((threads + 255) / 256)),
+                           dim3(256), 0, stream, p.part_o, p.part_l, p.o, p.lse, rows,
+                           a.splits);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((decode_kernel<E, D, CAUSAL, false>), dim3(units), dim3(256), 0, stream,
+                       p);
+    return hipGetLastError();
+}
+
 template <typename E, int D, bool CAUSAL, bool VARLEN, bool SPLIT, bool DROP = false>
 hipError_t run_fwd(const FwdArgs& a, hipStream_t stream) {
     using T = FwdTile<D>;
@@ -583,6 +866,8 @@ hipError_t run_fwd(const FwdArgs& a, hipStream_t stream) {
 
 template <typename E, int D>
 hipError_t run_fwd_d(const FwdArgs& a, hipStream_t stream) {
+    if (a.decode)
+        return a.causal ? run_decode<E, D, true>(a, stream) : run_decode<E, D, false>(a, stream);
     const bool varlen = a.cu != nullptr;
     if (a.drop.thresh > 0)  // dropout: dense batch only
         return a.causal ? run_fwd<E, D, true, false, false, true>(a, stream)

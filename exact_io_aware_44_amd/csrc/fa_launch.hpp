@@ -36,6 +36,7 @@ struct FwdArgs {
     float* part = nullptr;  // split workspace: partial O, then partial L (fp32)
     bool f16 = false;       // element type: bf16, or fp16 when set
     Dropout drop{};         // thresh 0: no dropout
+    bool decode = false;    // N <= 32 queries per (batch, head): decoding kernel
 };
 
 struct BwdArgs {

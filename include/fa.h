@@ -130,9 +130,13 @@ size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int D, int nu
  * arguments, up to rounding.
  *
  *   q, k, v, o, lse, B, H, Nq, Nk, D, causal   as for fa_fwd_qk
- *   num_splits  0 = choose automatically (about 512 workgroups in total,
- *               ranges of at least 256 keys); > 0 = that many ranges, at
- *               most one per 64 keys.  With one range no workspace is used.
+ *   num_splits  0 = choose automatically; > 0 = that many ranges, at most
+ *               one per 64 keys.  With one range no workspace is used.
+ *               Nq <= 32 runs a decoding kernel (one workgroup per range and
+ *               head, its four waves streaming 32-key blocks; automatic
+ *               choice: about 256 workgroups, ranges of at least 512 keys).
+ *               Larger Nq runs the forward tiles over each range (automatic
+ *               choice: about 512 workgroups, ranges of at least 256 keys).
  *   workspace   device memory of fa_fwd_splitkv_workspace_size(B, H, Nq, Nk,
  *               D, num_splits) bytes (may be NULL when that is 0); contents
  *               on entry ignored, on exit unspecified

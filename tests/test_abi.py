@@ -112,9 +112,13 @@ def test_splitkv_rejects(lib, kw, code):
 
 def test_splitkv_workspace_size():
     ws = fa.fa_fwd_splitkv_workspace_size
-    # B2 H4 Nq1 Nk4096: automatic count min(128, 512/8, 4096/256) = 16 ranges
-    # of 256 keys; partial O (16*8 rows * 128 fp32) then partial L (padded)
-    assert ws(2, 4, 1, 4096, 128) == 4 * (16 * 8 * 128 + 128)
+    # B2 H4 Nq1 Nk4096 (decoding kernel): automatic count min(128, 256/8,
+    # 4096/512) = 8 ranges of 512 keys; partial O (8*8 rows * 128 fp32) then
+    # partial L (padded to 64 floats)
+    assert ws(2, 4, 1, 4096, 128) == 4 * (8 * 8 * 128 + 64)
+    # B2 H4 Nq64 Nk4096 (forward tiles): min(128, 512/8, 4096/256) = 16 ranges
+    # of 256 keys; partial O (16*8*64 rows * 128 fp32) then partial L
+    assert ws(2, 4, 64, 4096, 128) == 4 * (16 * 8 * 64 * 128 + 16 * 8 * 64)
     assert ws(2, 4, 1, 4096, 128, 4) == 4 * (4 * 8 * 128 + 64)
     assert ws(2, 4, 1, 4096, 128, 1) == 0       # one range: plain forward
     assert ws(64, 32, 1, 200, 128) == 0         # enough heads and a short cache

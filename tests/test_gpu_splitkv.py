@@ -21,6 +21,11 @@ CASES = [  # (B, H, Nq, Nk, D, num_splits): single key, ragged ranges, many rang
     (2, 2, 1, 1000, 128, 0), (1, 4, 1, 4097, 128, 7), (1, 2, 1, 4097, 64, 64),
     (2, 2, 4, 3000, 128, 0), (1, 2, 16, 2048, 64, 5), (1, 2, 130, 70, 128, 2),
     (1, 1, 200, 5000, 128, 0), (1, 2, 3, 640, 128, 1),
+    # decoding kernel limits: 32 queries (largest) and 33 (forward tiles),
+    # fewer keys than queries (dead rows under the causal mask), fewer
+    # blocks than waves, a ragged range end with several ranges
+    (1, 2, 32, 700, 128, 0), (1, 2, 33, 700, 128, 0), (1, 3, 16, 5, 64, 0),
+    (2, 1, 2, 70, 128, 1), (2, 2, 7, 100, 128, 3),
 ]
 
 
