@@ -6,7 +6,9 @@ D128 bf16 (iid N(0,1) inputs, scale 1/sqrt(128)), inputs resident in HBM.
 Prints ONE JSON line with the throughput in TFLOP/s, the roofline position of
 the forward kernel, the backward pass (fa_bwd, B2 H32 N4096 D128 causal)
 against the same roofline, the decoding-shaped forward (fa_fwd_splitkv, one
-query against a 16384-token cache, B8 H32 D128) against HBM bandwidth, and
+query against a 16384-token cache, B8 H32 D128) against HBM bandwidth, the
+varlen (16 packed causal sequences) and long-context (B1 H32 N65536)
+forwards, the metric workload with L2/MALL flushed before each launch, and
 the fp64 CPU oracle timed on a bounded sample of the same workload.
 
 FLOP convention: 4*D flops per (query, key) pair, causal counted as half of
@@ -173,6 +175,83 @@ def run_decode(torch, ai, fa, steps):
             "launches": 2 if ws_bytes else 1}
 
 
+def gpu_randn_bf16(torch, shape, seed):
+    """Seeded iid N(0,1) fp32 drawn on the GPU, rounded to bf16 (timing-only
+    inputs: same shape and distribution as the parity inputs, generated
+    where they are used)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+
+def run_other_configs(torch, ai, fa, steps):
+    """The varlen and long-context forward workloads, same roofline."""
+    out = {}
+    # varlen: 16 causal sequences, lengths U[128, 8192], packed [H, total, D]
+    lengths = ai.varlen_lengths(ai.VARLEN_LENGTH_SEED)
+    cu = ai.cu_seqlens(lengths).cuda()
+    total, H, D = int(sum(lengths)), ai.VARLEN_H, ai.VARLEN_D
+    log("varlen: %d sequences, %d tokens" % (len(lengths), total))
+    q, k, v = (gpu_randn_bf16(torch, (H, total, D), ai.VARLEN_DATA_SEED * 10 + i)
+               for i in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty((H, total), dtype=torch.float32, device="cuda")
+    scale = ai.default_scale(D)
+
+    def vstep():
+        fa.fa_fwd_varlen(q, k, v, cu, max(lengths), softmax_scale=scale, causal=True,
+                         out=o, lse=lse)
+
+    _, per = time_launches(torch, vstep, steps, 3)
+    flops = sum(4.0 * H * D * n * n * 0.5 for n in lengths)
+    out["varlen"] = launch_stats(ai.VARLEN_NAME, flops, per)
+    del q, k, v, o, lse
+    # long context: B1 H32 N65536 D128 causal
+    w = ai.LONG
+    log("long:", w.name)
+    q, k, v = (gpu_randn_bf16(torch, (w.B, w.H, w.N, w.D), w.seed * 10 + i) for i in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+
+    def lstep():
+        fa.fa_fwd(q, k, v, softmax_scale=w.scale, causal=True, out=o, lse=lse)
+
+    _, per = time_launches(torch, lstep, max(2, steps // 2), 1)
+    out["long"] = launch_stats(w.name, fwd_flops(w.B, w.H, w.N, w.D, True), per)
+    del q, k, v, o, lse
+    return out
+
+
+def launch_stats(name, flops, per):
+    """Per-launch median / min / mean of HIP-event durations (ms) and the
+    TFLOP/s of the median against the bf16 peak."""
+    med = statistics.median(per)
+    return {"workload": name, "launches": len(per), "ms_median": round(med, 4),
+            "ms_min": round(min(per), 4), "ms_mean": round(statistics.mean(per), 4),
+            "tflops": round(flops / (med * 1e-3) / 1e12, 1),
+            "frac": round(flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def run_cold_l2(torch, fwd_step, flops, steps):
+    """The metric workload with L2/MALL flushed before each launch: a
+    512 MiB scratch write runs between launches and only the attention
+    launch is timed."""
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    per = []
+    for i in range(steps + 1):
+        scratch.fill_(i & 0xFF)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fwd_step()
+        e.record()
+        torch.cuda.synchronize()
+        if i > 0:
+            per.append(s.elapsed_time(e))
+    del scratch
+    return launch_stats("causal fwd B4 H32 N4096 D128, L2/MALL flushed before each launch",
+                        flops, per)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +259,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--bwd-steps", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--config-steps", type=int, default=10,
+                    help="launches of the varlen and long workloads and of the "
+                         "flushed-cache run (0 = skip)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -227,6 +309,8 @@ def main(argv=None):
     value = flops / (ms_per_step * 1e-3) / 1e12
     launch_ms = statistics.mean(per)
     achieved = flops / (launch_ms * 1e-3) / 1e12
+    forward_launches = launch_stats(w.name, flops, per)
+    cold = run_cold_l2(torch, fwd_step, flops, args.config_steps) if args.config_steps > 0 else None
     del q, k, v, o, lse
 
     # ---- backward against the same roofline ---------------------------------
@@ -236,6 +320,7 @@ def main(argv=None):
     decode = None
     if args.decode_steps > 0:
         decode = run_decode(torch, ai, fa, args.decode_steps)
+    others = run_other_configs(torch, ai, fa, args.config_steps) if args.config_steps > 0 else {}
 
     line = {
         "metric": METRIC,
@@ -261,8 +346,12 @@ def main(argv=None):
                      "traffic": measured_traffic(),
                      "kernel": "fwd_kernel<128, causal>",
                      "avg_launch_ms": round(launch_ms, 5)},
+        "forward_launches": forward_launches,
+        "forward_cold_l2": cold,
         "backward": backward,
         "decode": decode,
+        "varlen": others.get("varlen"),
+        "long": others.get("long"),
     }
     if rank == 0 and args.cpu_budget > 0:
         log("cpu baseline (oracle), about %.0f s" % args.cpu_budget)

@@ -66,15 +66,6 @@ __device__ __forceinline__ void load4_lds(Buf b, uint32_t off, void* lds_wave_ba
 // s_waitcnt vmcnt(0) lgkmcnt(0): this wave's loads (global and LDS) are done.
 __device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0070); }
 
-// Workgroup i of a 1-D grid runs on XCD i % 8; this remap gives each XCD a
-// contiguous, head-major range of units so one head's tiles stay in one L2.
-__device__ __forceinline__ void unit_of(int i, int total, int per_head, int& head,
-                                        int& idx) {
-    const int L = (total & 7) == 0 ? (i & 7) * (total >> 3) + (i >> 3) : i;
-    head = L / per_head;
-    idx = L - head * per_head;
-}
-
 // ---------------------------------------------------------------------------
 // 1. Per-row constants: D_i = dO_i . O_i (fp32 sum of exact bf16 products)
 //    and -L_i log2(e), the exponent offset that turns a score into its weight.

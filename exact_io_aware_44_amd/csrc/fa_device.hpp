@@ -83,6 +83,23 @@ __device__ __forceinline__ void load16_lds(Buf b, uint32_t off, void* lds_wave_b
     __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (FA_LDS void*)lds_wave_base, 16, off,
                                              0, 0, 0);
 }
+// Unit schedule of a 1-D grid of `total` = heads * per_head workgroups.
+// Workgroup i runs on XCD i % 8.  XCD x takes heads x, x + 8, x + 16, ... in
+// order, all units of a head together, so one head's K/V re-reads stay in
+// one XCD's L2, and heads of unequal work (the sequences of a packed batch
+// are consecutive heads) spread evenly over the eight XCDs.
+__device__ __forceinline__ void unit_of(int i, int total, int per_head, int& head, int& idx) {
+    const int heads = total / per_head;
+    if ((heads & 7) == 0) {
+        const int s = i >> 3, k = s / per_head;
+        head = (i & 7) + 8 * k;
+        idx = s - k * per_head;
+    } else {
+        head = i / per_head;
+        idx = i - head * per_head;
+    }
+}
+
 // Offset that is out of range for every buffer (all buffers are < 2 GiB).
 constexpr uint32_t kOutOfRange = 0x80000000u;
 // s_waitcnt vmcnt(0) only (gfx9 encoding: expcnt and lgkmcnt left at max).

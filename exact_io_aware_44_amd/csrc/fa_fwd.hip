@@ -111,16 +111,6 @@ struct FwdParams {
     Dropout drop;  // attention dropout (dense forward only)
 };
 
-// Unit schedule.  Workgroup i of a 1-D grid is dispatched to XCD i % 8; the
-// remap below gives each XCD a contiguous range of units, head-major, so the
-// K/V re-reads of one head stay in that XCD's L2.
-__device__ __forceinline__ void unit_of(int i, int total, int per_head, int& head,
-                                        int& idx) {
-    const int L = (total & 7) == 0 ? (i & 7) * (total >> 3) + (i >> 3) : i;
-    head = L / per_head;
-    idx = L - head * per_head;
-}
-
 using True = std::true_type;
 using False = std::false_type;
 
