@@ -233,14 +233,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     // P = exp2(S c - L log2 e) and dS = P (dP - D), rounded to bf16 in the
     // B-operand order of the two 16-query k-steps; MASK zeroes the weights
     // of keys after their query (tiles on the causal diagonal only).
-    auto weights = [&](const float* __restrict__ fs, int qb0, int b, const f32x16& s,
-                       const f32x16& dp, bf16x8* pb, bf16x8* sb, auto mask_tag)
-                       __attribute__((always_inline)) {
+    auto weights_group = [&](const float* __restrict__ fs, int qb0, int b, const f32x16& s,
+                             const f32x16& dp, float* pf, float* sf, int a, auto mask_tag)
+                             __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int tm = kj - qb0 - 4 * hi;  // masked where tm > local query offset
-        float pf[16], sf[16];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
+        {
             const f32x4 nl = *reinterpret_cast<const f32x4*>(fs + 32 * b + 8 * a + 4 * hi);
             const f32x4 dd =
                 *reinterpret_cast<const f32x4*>(fs + T::BQ + 32 * b + 8 * a + 4 * hi);
@@ -265,6 +263,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
                 }
             }
         }
+    };
+    auto weights = [&](const float* __restrict__ fs, int qb0, int b, const f32x16& s,
+                       const f32x16& dp, bf16x8* pb, bf16x8* sb, auto mask_tag)
+                       __attribute__((always_inline)) {
+        float pf[16], sf[16];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) weights_group(fs, qb0, b, s, dp, pf, sf, a, mask_tag);
         pb[0] = pack8<E>(pf);
         pb[1] = pack8<E>(pf + 8);
         sb[0] = pack8<E>(sf);
@@ -293,9 +298,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
 
     // One 64-query stage.  MASKED: a stage on the causal diagonal of this
     // wave's keys (blocks wholly before the keys are skipped, the rest
-    // masked); otherwise both blocks run straight through, block 1's products
-    // issued before block 0's weights so the matrix unit stays busy while the
-    // exponentials run.
+    // masked, block by block); otherwise a software-pipelined pass over both
+    // blocks (see below).
     auto step = [&](int qt, bool more, const bf16* __restrict__ qs,
                     const bf16* __restrict__ dos, const float* __restrict__ fs,
                     bf16* __restrict__ qn, bf16* __restrict__ don, float* __restrict__ fn,
@@ -306,14 +310,75 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
         f32x16 s0, dp0;
         bf16x8 pb0[2], sb0[2];
         if constexpr (!MASKED) {
+            // Software pipeline of the stage: every MFMA operand is read from
+            // LDS PF MFMAs ahead; block 0's weights run beside block 1's
+            // score MFMAs, block 1's weights beside block 0's dV/dK MFMAs.
+            constexpr int PF = 6;
             f32x16 s1, dp1;
             bf16x8 pb1[2], sb1[2];
-            scores(qs, dos, 0, s0, dp0);
-            scores(qs, dos, 1, s1, dp1);
+            // phase 1: S and dP of both blocks (i: block i / 2DS, k-step
+            // (i % 2DS) / 2, S when even, dP when odd)
+            constexpr int NSC = 4 * T::DS;
+            auto sc_fetch = [&](int i) {
+                const int b = i / (2 * T::DS), ss = (i % (2 * T::DS)) >> 1;
+                return lds_read16(((i & 1) ? dos : qs) + qd_off<D>(32 * b + l32, 2 * ss + hi));
+            };
+            s0 = dp0 = s1 = dp1 = f32x16{};
+            bf16x8 op[NSC];
+#pragma unroll
+            for (int i = 0; i < PF; ++i) op[i] = sc_fetch(i);
+#pragma unroll
+            for (int i = 0; i < NSC; ++i) {
+                if (i + PF < NSC) op[i + PF] = sc_fetch(i + PF);
+                const int b = i / (2 * T::DS), ss = (i % (2 * T::DS)) >> 1;
+                if (b == 0) {
+                    if (i & 1) dp0 = mfma32<E>(op[i], vreg[ss], dp0);
+                    else s0 = mfma32<E>(op[i], kreg[ss], s0);
+                } else {
+                    if (i & 1) dp1 = mfma32<E>(op[i], vreg[ss], dp1);
+                    else s1 = mfma32<E>(op[i], kreg[ss], s1);
+                }
+            }
             weights(fs, q0, 0, s0, dp0, pb0, sb0, False{});
-            accumulate(qs, dos, 0, pb0, sb0);
-            weights(fs, q0 + 32, 1, s1, dp1, pb1, sb1, False{});
-            accumulate(qs, dos, 1, pb1, sb1);
+            // phases 2 and 3: dV^T += dO^T P and dK^T += Q^T dS per block
+            // (j: d-block j / 4, k-step (j / 2) % 2, dV when even, dK when
+            // odd); transpose operands PF ahead
+            constexpr int NAC = 4 * T::DB;
+            auto ac_fetch = [&](int b, int j) {
+                const int e = j >> 2, t = (j >> 1) & 1;
+                const int rr = 32 * b + 16 * t + 4 * hi + (i16 >> 2);
+                const int cc = 4 * e + 2 * (g & 1) + ((i16 & 3) >> 1);
+                const bf16* src = (j & 1) ? qs : dos;
+                return cat(lds_read_tr(src + qd_off<D>(rr, cc) + 4 * (i16 & 1)),
+                           lds_read_tr(src + qd_off<D>(rr + 8, cc) + 4 * (i16 & 1)));
+            };
+            float pf1[16], sf1[16];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const bf16x8* pb = b ? pb1 : pb0;
+                const bf16x8* sb = b ? sb1 : sb0;
+                bf16x8 ao[NAC];
+#pragma unroll
+                for (int j = 0; j < PF; ++j) ao[j] = ac_fetch(b, j);
+#pragma unroll
+                for (int j = 0; j < NAC; ++j) {
+                    if (j + PF < NAC) ao[j + PF] = ac_fetch(b, j + PF);
+                    const int e = j >> 2, t = (j >> 1) & 1;
+                    if (j & 1) mfma_acc<E>(dk[e], ao[j], sb[t]);
+                    else mfma_acc<E>(dv[e], ao[j], pb[t]);
+                    // block 1's weights: its four groups of 4 queries spread
+                    // evenly over block 0's MFMAs
+                    constexpr int GAP = NAC / 4;
+                    if (b == 0 && j % GAP == GAP - 1)
+                        weights_group(fs, q0 + 32, 1, s1, dp1, pf1, sf1, j / GAP, False{});
+                }
+                if (b == 0) {
+                    pb1[0] = pack8<E>(pf1);
+                    pb1[1] = pack8<E>(pf1 + 8);
+                    sb1[0] = pack8<E>(sf1);
+                    sb1[1] = pack8<E>(sf1 + 8);
+                }
+            }
         } else {
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
