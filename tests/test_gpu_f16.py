@@ -51,7 +51,10 @@ def test_varlen_qk_splitkv(gpu):
     o_ref, l_ref = oracle.fwd_varlen(q, k, v, cu, ai.default_scale(D), True)
     check_fwd(o, lse, o_ref, l_ref, "f16 varlen")
     q, k, v = _r((2, 2, 5, D), 1210), _r((2, 2, 3000, D), 1211), _r((2, 2, 3000, D), 1212)
-    for fn, kw in ((gpu.fa_fwd_qk, {}), (gpu.fa_fwd_splitkv, dict(num_splits=5))):
+    # fa_fwd_splitkv with 5 queries runs the decoding kernel: several ranges
+    # (partials merged), one range (O and L written directly), automatic
+    for fn, kw in ((gpu.fa_fwd_qk, {}), (gpu.fa_fwd_splitkv, dict(num_splits=5)),
+                   (gpu.fa_fwd_splitkv, dict(num_splits=1)), (gpu.fa_fwd_splitkv, {})):
         o, lse = fn(q.cuda(), k.cuda(), v.cuda(), causal=True, **kw)
         torch.cuda.synchronize()
         o_ref, l_ref = oracle.fwd_qk(q, k, v, ai.default_scale(D), True)
