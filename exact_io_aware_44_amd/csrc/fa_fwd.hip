@@ -547,11 +547,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* part_o, const f
 //  - K and V blocks are read with ordinary wave-wide loads of 1 KiB of
 //    consecutive rows into registers, two blocks ahead, so each CU keeps
 //    128 KiB in flight.  (Loading the MFMA operands themselves touches 32
-//    rows per load, 32 bytes each, and streams at about half the rate; the
-//    global->LDS DMA path tops out near 6.1 TB/s on this chip, plain loads
-//    near 7.)  A block is then written into the wave's own LDS region,
+//    rows per load, 32 bytes each; alone, that pattern streams at about
+//    3.8 TB/s.)  A block is then written into the wave's own LDS region,
 //    K rows padded and V rows swizzled as in fwd_kernel, and read back as
-//    MFMA operands;
+//    MFMA operands.  (Filling the LDS by global->LDS DMA instead measured
+//    the same on this workload: about 6 TB/s is what per-head streams of
+//    this layout reach on this chip, with or without arithmetic.)
 //  - at the end the waves' (m, l, u) are merged through LDS by the same
 //    running-softmax rule, then O and L (or the range's partials) are stored.
 template <int D>
