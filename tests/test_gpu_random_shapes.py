@@ -1,0 +1,105 @@
+"""GPU parity on seeded random shapes: every entry point against the fp64
+oracle on sizes drawn from a fixed generator (odd lengths, ragged tiles,
+single rows, empty varlen sequences, more queries than keys), so that cases
+between the hand-picked ones are covered too."""
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as ai
+import oracle
+from _parity import GRAD_REL_L2, check_fwd, f64, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+_RNG = np.random.default_rng(20260)
+
+
+def _draw(n, lo, hi):
+    return [int(x) for x in _RNG.integers(lo, hi + 1, size=n)]
+
+
+# (B, H, N, D, causal) for the dense forward and backward
+DENSE = [(int(b), int(h), int(n), int(d), bool(c)) for b, h, n, d, c in zip(
+    _draw(12, 1, 2), _draw(12, 1, 3), _draw(12, 1, 700), _RNG.choice([64, 128], 12),
+    _RNG.integers(0, 2, 12))]
+# (B, H, Nq, Nk, D, causal, num_splits) for the unequal-length and split paths
+# (half the query counts fall in the decoding kernel's range, at most 32;
+# some key counts are smaller than the query counts)
+QK = [(int(b), int(h), int(nq), int(nk), int(d), bool(c), int(s)) for b, h, nq, nk, d, c, s in zip(
+    _draw(12, 1, 2), _draw(12, 1, 2), _draw(6, 1, 32) + _draw(6, 33, 300),
+    _draw(4, 1, 1500) + _draw(2, 1, 40) + _draw(4, 1, 1500) + _draw(2, 1, 40),
+    _RNG.choice([64, 128], 12), _RNG.integers(0, 2, 12), _draw(12, 0, 9))]
+# varlen: sequence lengths (zeros allowed), heads, width, causal
+VARLEN = [([int(x) for x in _RNG.integers(0, 400, size=int(ns))], int(h), int(d), bool(c))
+          for ns, h, d, c in zip(_draw(6, 1, 7), _draw(6, 1, 3), _RNG.choice([64, 128], 6),
+                                 _RNG.integers(0, 2, 6))]
+VARLEN[0] = ([0] + VARLEN[0][0] + [0], *VARLEN[0][1:])  # empty sequences at both ends
+
+
+@pytest.mark.parametrize("case", DENSE, ids=lambda c: "B%dH%dN%dD%dc%d" % c)
+def test_dense_forward(gpu, case):
+    B, H, N, D, causal = case
+    say("case", case)
+    q, k, v = ai.qkv(B, H, N, D, 3000 + N)
+    scale = ai.default_scale(D)
+    o, lse = gpu.fa_fwd(q.cuda(), k.cuda(), v.cuda(), softmax_scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.fwd(q, k, v, scale, causal)
+    check_fwd(o, lse, o_ref, l_ref, str(case))
+
+
+@pytest.mark.parametrize("case", DENSE[:8], ids=lambda c: "B%dH%dN%dD%dc%d" % c)
+def test_dense_backward(gpu, case):
+    B, H, N, D, causal = case
+    say("case", case)
+    q, k, v = ai.qkv(B, H, N, D, 4000 + N)
+    do = ai.randn_bf16((B, H, N, D), 4100 + N)
+    scale = ai.default_scale(D)
+    qc, kc, vc, doc = (x.cuda() for x in (q, k, v, do))
+    o, lse = gpu.fa_fwd(qc, kc, vc, softmax_scale=scale, causal=causal)
+    grads = gpu.fa_bwd(qc, kc, vc, o, lse, doc, softmax_scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    refs = oracle.bwd(q, k, v, do, scale, causal)
+    for name, g, r in zip(("dQ", "dK", "dV"), grads, refs):
+        e = rel_l2(g, r)
+        say("  %s rel-L2 %.3e" % (name, e))
+        assert torch.isfinite(g).all() and e <= GRAD_REL_L2, (case, name, e)
+
+
+@pytest.mark.parametrize("case", QK, ids=lambda c: "B%dH%dNq%dNk%dD%dc%ds%d" % c)
+def test_unequal_and_split(gpu, case):
+    B, H, Nq, Nk, D, causal, ns = case
+    say("case", case)
+    q = ai.randn_bf16((B, H, Nq, D), 5000 + Nq)
+    k = ai.randn_bf16((B, H, Nk, D), 5001 + Nk)
+    v = ai.randn_bf16((B, H, Nk, D), 5002 + Nk)
+    scale = ai.default_scale(D)
+    o_ref, l_ref = oracle.fwd_qk(q, k, v, scale, causal)
+    dead = np.isneginf(l_ref)  # queries before the first key (causal, Nq > Nk)
+    for name, fn, kw in (("qk", gpu.fa_fwd_qk, {}),
+                         ("splitkv", gpu.fa_fwd_splitkv, dict(num_splits=ns))):
+        o, lse = fn(q.cuda(), k.cuda(), v.cuda(), softmax_scale=scale, causal=causal, **kw)
+        torch.cuda.synchronize()
+        og, lg = f64(o), f64(lse)
+        assert (og[dead] == 0).all() and np.isneginf(lg[dead]).all(), (case, name)
+        check_fwd(og[~dead], lg[~dead], o_ref[~dead], l_ref[~dead], "%s %s" % (name, case))
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: "n%dH%dD%dc%d" % (len(c[0]), c[1], c[2], c[3]))
+def test_varlen(gpu, case):
+    lengths, H, D, causal = case
+    say("case", case)
+    total = sum(lengths)
+    if total == 0:
+        lengths = lengths[:-1] + [1]
+        total = 1
+    cu = ai.cu_seqlens(lengths)
+    g = ai.generator(6000 + total)
+    q, k, v = (ai.randn_bf16((H, total, D), g) for _ in range(3))
+    scale = ai.default_scale(D)
+    o, lse = gpu.fa_fwd_varlen(q.cuda(), k.cuda(), v.cuda(), cu.cuda(), max(max(lengths), 1),
+                               softmax_scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.fwd_varlen(q, k, v, cu, scale, causal)
+    check_fwd(o, lse, o_ref, l_ref, str(case))
