@@ -42,6 +42,7 @@
 //    same head so all units carry equal work.
 //  - A 1-D grid is remapped so that each XCD owns whole heads (their K/V
 //    re-reads hit its private L2).
+#include <algorithm>
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -109,7 +110,36 @@ struct FwdParams {
     float* part_o;
     float* part_l;
     Dropout drop;  // attention dropout (dense forward only)
+    // dense causal: the last `tail` heads of each XCD are issued as single
+    // query tiles, heaviest first (0: every unit is a pair of tiles)
+    int tail;
 };
+
+// Dense causal schedule with a split tail.  Units of equal work (pairs of a
+// light and a heavy query tile) finish at scattered times, so the last round
+// of a plain pair schedule leaves CUs idle.  Here XCD x still takes heads
+// x, x + 8, ... in order, all units of a head together, but its last `tail`
+// heads come as single query tiles ordered from the heaviest down, which
+// fills the end of the launch with ever smaller units.  Returns the head and
+// either the pair index (rank < 0) or the single tile's rank from the
+// heaviest (rank >= 0).
+__device__ __forceinline__ void tail_unit(int i, int heads, int per_head, int tail,
+                                          int& head, int& uidx, int& rank) {
+    const int x = i & 7, s = i >> 3;
+    const int hx = heads >> 3;                      // heads per XCD
+    const int lead = (hx - tail) * per_head;        // pair units before the tail
+    if (s < lead) {
+        const int k = s / per_head;
+        head = x + 8 * k;
+        uidx = s - k * per_head;
+        rank = -1;
+    } else {
+        const int s2 = s - lead;
+        head = x + 8 * (hx - tail + s2 % tail);
+        uidx = 0;
+        rank = s2 / tail;
+    }
+}
 
 using True = std::true_type;
 using False = std::false_type;
@@ -129,8 +159,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int l32 = lane & 31, hi = lane >> 5;
     const int g = lane >> 4, i16 = lane & 15;
-    int head, uidx;
-    unit_of(blockIdx.x, gridDim.x, p.per_head, head, uidx);
+    int head, uidx, rank = -1;
+    if (CAUSAL && !SPLIT && !VARLEN && p.tail > 0)
+        tail_unit(blockIdx.x, p.heads, p.per_head, p.tail, head, uidx, rank);
+    else
+        unit_of(blockIdx.x, gridDim.x, p.per_head, head, uidx);
     const int b = head / p.H, h = head - b * p.H;
     int split = 0;
     if constexpr (SPLIT) {
@@ -166,7 +199,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     // the query tiles of this unit, heavy first; ntiles is workgroup-uniform
     const int n_tiles = (n + T::BR - 1) / T::BR;
     int tile0 = uidx, tile1 = -1;
-    if (CAUSAL && !SPLIT) {
+    if (CAUSAL && !SPLIT && rank >= 0) {
+        tile0 = n_tiles - 1 - rank;  // a single tile of the split tail
+        if (tile0 < 0) return;
+    } else if (CAUSAL && !SPLIT) {
         tile0 = n_tiles - 1 - uidx;
         tile1 = uidx;
         if (tile1 > tile0) return;  // past the middle of this sequence's tiles
@@ -855,8 +891,15 @@ hipError_t run_fwd(const FwdArgs& a, hipStream_t stream) {
     const int64_t rows = (int64_t)a.B * a.H * a.N;
     p.part_o = a.part;
     p.part_l = a.part + ((rows * a.splits * D + 63) & ~(int64_t)63);
-    const int64_t units = (int64_t)p.per_head * a.H * a.B;
+    int64_t units = (int64_t)p.per_head * a.H * a.B;
     p.drop = a.drop;
+    p.tail = 0;
+    if (CAUSAL && !SPLIT && !VARLEN && (p.heads & 7) == 0) {
+        // about one round of the XCD's 64 workgroup slots as single tiles
+        const int hx = p.heads >> 3;
+        p.tail = std::min(hx, (64 + p.per_head - 1) / p.per_head);
+        units = 8 * ((int64_t)(hx - p.tail) * p.per_head + (int64_t)p.tail * n_qt);
+    }
     hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, VARLEN, SPLIT, DROP>), dim3((unsigned)units),
                        dim3(T::THREADS), 0, stream, p);
     if (!SPLIT) return hipGetLastError();
