@@ -115,31 +115,6 @@ struct FwdParams {
     int tail;
 };
 
-// Dense causal schedule with a split tail.  Units of equal work (pairs of a
-// light and a heavy query tile) finish at scattered times, so the last round
-// of a plain pair schedule leaves CUs idle.  Here XCD x still takes heads
-// x, x + 8, ... in order, all units of a head together, but its last `tail`
-// heads come as single query tiles ordered from the heaviest down, which
-// fills the end of the launch with ever smaller units.  Returns the head and
-// either the pair index (rank < 0) or the single tile's rank from the
-// heaviest (rank >= 0).
-__device__ __forceinline__ void tail_unit(int i, int heads, int per_head, int tail,
-                                          int& head, int& uidx, int& rank) {
-    const int x = i & 7, s = i >> 3;
-    const int hx = heads >> 3;                      // heads per XCD
-    const int lead = (hx - tail) * per_head;        // pair units before the tail
-    if (s < lead) {
-        const int k = s / per_head;
-        head = x + 8 * k;
-        uidx = s - k * per_head;
-        rank = -1;
-    } else {
-        const int s2 = s - lead;
-        head = x + 8 * (hx - tail + s2 % tail);
-        uidx = 0;
-        rank = s2 / tail;
-    }
-}
 
 using True = std::true_type;
 using False = std::false_type;
