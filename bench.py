@@ -35,7 +35,7 @@ PEAK_BF16_TFLOPS = 2516.6
 HBM_GBS = 8000.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_causal_b4h32n4096d128_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_io_aware_44_amd", "csrc", f)
-                  for f in ("fa_fwd.hip", "fa_device.hpp")]
+                  for f in ("fa_fwd.hip", "fa_device.hpp", "fa_schedule.hpp")]
 
 
 def log(*a):

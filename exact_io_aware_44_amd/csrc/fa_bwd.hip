@@ -170,14 +170,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     const int nkt = (n + T::BK - 1) / T::BK;
     // key tiles of this unit: under causal masking a heavy one (many queries
     // follow it) and the matching light one, so all units carry equal work
-    int kt0 = uidx, kt1 = -1;
-    if (CAUSAL) {
-        kt1 = nkt - 1 - uidx;
-        if (kt1 < kt0) return;
-        if (kt1 == kt0) kt1 = -1;
-    } else if (kt0 >= nkt) {
-        return;
-    }
+    int kt0, kt1;
+    if (!unit_tiles(CAUSAL, false, uidx, nkt, kt0, kt1)) return;
 
     const int64_t row0 = (int64_t)head * n;
     const uint32_t bytes = (uint32_t)n * D * 2;
@@ -489,15 +483,8 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
     const int nqt = (n + T::BR - 1) / T::BR;
     // query tiles of this unit: under causal masking a heavy one (late, many
     // keys) and the matching light one
-    int t0 = uidx, t1 = -1;
-    if (CAUSAL) {
-        t0 = nqt - 1 - uidx;
-        t1 = uidx;
-        if (t1 > t0) return;
-        if (t1 == t0) t1 = -1;
-    } else if (t0 >= nqt) {
-        return;
-    }
+    int t0, t1;
+    if (!unit_tiles(CAUSAL, true, uidx, nqt, t0, t1)) return;
 
     const int64_t row0 = (int64_t)head * n;
     const uint32_t bytes = (uint32_t)n * D * 2;

@@ -25,6 +25,7 @@
 #include <stdint.h>
 
 #include "fa_launch.hpp"  // Dropout
+#include "fa_schedule.hpp"
 
 namespace fa {
 
@@ -83,49 +84,6 @@ __device__ __forceinline__ void load16_lds(Buf b, uint32_t off, void* lds_wave_b
     __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (FA_LDS void*)lds_wave_base, 16, off,
                                              0, 0, 0);
 }
-// Unit schedule of a 1-D grid of `total` = heads * per_head workgroups.
-// Workgroup i runs on XCD i % 8.  XCD x takes heads x, x + 8, x + 16, ... in
-// order, all units of a head together, so one head's K/V re-reads stay in
-// one XCD's L2, and heads of unequal work (the sequences of a packed batch
-// are consecutive heads) spread evenly over the eight XCDs.
-__device__ __forceinline__ void unit_of(int i, int total, int per_head, int& head, int& idx) {
-    const int heads = total / per_head;
-    if ((heads & 7) == 0) {
-        const int s = i >> 3, k = s / per_head;
-        head = (i & 7) + 8 * k;
-        idx = s - k * per_head;
-    } else {
-        head = i / per_head;
-        idx = i - head * per_head;
-    }
-}
-
-// Causal schedule with a split tail.  Units of equal work (pairs of a light
-// and a heavy tile) finish at scattered times, so the last round of a plain
-// pair schedule ends raggedly.  Here XCD x still takes heads x, x + 8, ... in
-// order, all units of a head together (heads % 8 == 0), but its last `tail`
-// heads come as single tiles ordered from the heaviest down, which fills the
-// end of the launch with ever smaller units.  Returns the head and either the
-// pair index (rank < 0) or the single tile's rank from the heaviest
-// (rank >= 0).
-__device__ __forceinline__ void tail_unit(int i, int heads, int per_head, int tail,
-                                          int& head, int& uidx, int& rank) {
-    const int x = i & 7, s = i >> 3;
-    const int hx = heads >> 3;                      // heads per XCD
-    const int lead = (hx - tail) * per_head;        // pair units before the tail
-    if (s < lead) {
-        const int k = s / per_head;
-        head = x + 8 * k;
-        uidx = s - k * per_head;
-        rank = -1;
-    } else {
-        const int s2 = s - lead;
-        head = x + 8 * (hx - tail + s2 % tail);
-        uidx = 0;
-        rank = s2 / tail;
-    }
-}
-
 // Offset that is out of range for every buffer (all buffers are < 2 GiB).
 constexpr uint32_t kOutOfRange = 0x80000000u;
 // s_waitcnt vmcnt(0) only (gfx9 encoding: expcnt and lgkmcnt left at max).

@@ -173,18 +173,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     }
     // the query tiles of this unit, heavy first; ntiles is workgroup-uniform
     const int n_tiles = (n + T::BR - 1) / T::BR;
-    int tile0 = uidx, tile1 = -1;
-    if (CAUSAL && !SPLIT && rank >= 0) {
-        tile0 = n_tiles - 1 - rank;  // a single tile of the split tail
-        if (tile0 < 0) return;
-    } else if (CAUSAL && !SPLIT) {
-        tile0 = n_tiles - 1 - uidx;
-        tile1 = uidx;
-        if (tile1 > tile0) return;  // past the middle of this sequence's tiles
-        if (tile1 == tile0) tile1 = -1;
-    } else if (tile0 >= n_tiles) {
-        return;  // whole unit past the end of its sequence
-    }
+    int tile0, tile1;
+    if (!fwd_tiles(CAUSAL && !SPLIT, rank, uidx, n_tiles, tile0, tile1)) return;
     const int ntiles = tile1 >= 0 ? 2 : 1;
 
     const uint32_t bytes = (uint32_t)n * D * 2;
@@ -869,11 +859,10 @@ hipError_t run_fwd(const FwdArgs& a, hipStream_t stream) {
     int64_t units = (int64_t)p.per_head * a.H * a.B;
     p.drop = a.drop;
     p.tail = 0;
-    if (CAUSAL && !SPLIT && !VARLEN && (p.heads & 7) == 0) {
-        // about one round of the XCD's 64 workgroup slots as single tiles
-        const int hx = p.heads >> 3;
-        p.tail = std::min(hx, (64 + p.per_head - 1) / p.per_head);
-        units = 8 * ((int64_t)(hx - p.tail) * p.per_head + (int64_t)p.tail * n_qt);
+    if (CAUSAL && !SPLIT && !VARLEN) {
+        const FwdGrid grid = fwd_causal_grid(p.heads, n_qt);
+        p.tail = grid.tail;
+        units = grid.units;
     }
     hipLaunchKernelGGL((fwd_kernel<E, D, CAUSAL, VARLEN, SPLIT, DROP>), dim3((unsigned)units),
                        dim3(T::THREADS), 0, stream, p);
