@@ -180,8 +180,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     const uint32_t bytes = (uint32_t)n * D * 2;
     const uint32_t kbytes = (uint32_t)nk * D * 2;
     const Buf qb = make_buf(p.q + row0 * D, bytes);
-    const Buf kb = make_buf(p.k + (krow0 + kbeg) * D, kbytes);
-    const Buf vb = make_buf(p.v + (krow0 + kbeg) * D, kbytes);
     const Buf ob = make_buf(p.o + row0 * D, bytes);
     const Buf lb = p.lse ? make_buf(p.lse + row0, (uint32_t)n * 4)
                          : make_buf(nullptr, 0);
@@ -210,17 +208,31 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     const uint32_t voff = (uint32_t)((lane / T::CPR) * D +
                                      (((lane % T::CPR) ^ v_swz<D>(lane / T::CPR)) * 8)) * 2;
     static_assert(T::K_LOADS % 4 == 0 && T::V_LOADS % 4 == 0, "loads split evenly");
+    // A tile's origin moves the (scalar) buffer descriptor, not the per-lane
+    // offsets: its base advances and its range shrinks by k0 rows, so the
+    // range check still ends at the last key and the loop does no per-lane
+    // address arithmetic for the DMAs.
+    const bf16* kbase = p.k + (krow0 + kbeg) * D;
+    const bf16* vbase = p.v + (krow0 + kbeg) * D;
+    uint32_t voffx[VL];
+#pragma unroll
+    for (int x = 0; x < VL; ++x) voffx[x] = voff + (uint32_t)(T::RPL * (wave + 4 * x)) * D * 2;
+    auto tile_buf = [&](const bf16* base, int k0) {
+        // callers load only tiles that start before the last key: k0 < nk
+        const uint32_t rest = __builtin_amdgcn_readfirstlane(kbytes - (uint32_t)k0 * D * 2);
+        return make_buf(base + (size_t)k0 * D, rest);
+    };
     auto load_k = [&](int k0, bf16* dst) {
+        const Buf b = tile_buf(kbase, k0);
 #pragma unroll
         for (int x = 0; x < KL; ++x)
-            load16_lds(kb, koff[x] + (uint32_t)k0 * D * 2, dst + 512 * (wave + 4 * x));
+            load16_lds(b, koff[x], dst + 512 * (wave + 4 * x));
     };
     auto load_v = [&](int k0, bf16* dst) {
+        const Buf b = tile_buf(vbase, k0);
 #pragma unroll
-        for (int x = 0; x < VL; ++x) {
-            const int t = wave + 4 * x;
-            load16_lds(vb, voff + (uint32_t)(k0 + T::RPL * t) * D * 2, dst + 512 * t);
-        }
+        for (int x = 0; x < VL; ++x)
+            load16_lds(b, voffx[x], dst + 512 * (wave + 4 * x));
     };
 
     for (int rep = 0; rep < ntiles; ++rep) {
@@ -243,6 +255,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int e = 0; e < T::DB; ++e) acc[e] = f32x16{};
     float m_run = kNegInf, l_run = 0.f;  // l_run: this lane's half of the keys
+    float m_thr = kNegInf;                 // m_run + kLazyRescale
     float l_new = 0.f;                     // sum of the latest half's weights
 
     // ---- the pipeline works on 32-key half tiles: half h holds keys
@@ -264,20 +277,24 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
             if (8 * (r / 4) + (r & 3) >= lim) s[r] = kNegInf;
     };
 
-    // online softmax of one half: new running maximum (lazy), rescale factor,
-    // exponentials as bf16 B operands, row sum
-    auto softmax = [&](f32x16& s, bf16x8 (&pb)[2], float& alpha, bool& upd, int hsm) {
+    // online softmax of one half: new running maximum (lazy), exponentials as
+    // bf16 B operands, row sum.  m_use is the reference maximum the half's
+    // weights are taken against; the running state (m_run, m_thr) moves only
+    // in rescale(), whose branch runs on the rare half-steps where some
+    // lane's maximum grew.  CHK: the half may hold a row with no live key so
+    // far (only masked halves can), whose maximum is -inf.
+    auto softmax = [&](f32x16& s, bf16x8 (&pb)[2], float& m_use, bool& upd, int hsm,
+                       auto chk) {
+        constexpr bool CHK = decltype(chk)::value;
         float t4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             t4[i] = fmaxf(fmaxf(s[4 * i], s[4 * i + 1]), fmaxf(s[4 * i + 2], s[4 * i + 3]));
         float mx = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
         mx = pair_max(mx) * p.c;  // row maximum of the half, base-2 units
-        upd = mx > m_run + kLazyRescale;  // the first live half always moves it
+        upd = mx > m_thr;  // the first live half always moves it
         const float m_new = upd ? mx : m_run;
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;  // no key yet: no NaN
-        alpha = m_run - m_use;  // log2 of the rescale factor: 0 unless upd
-        m_run = m_new;
+        m_use = (CHK && m_new == kNegInf) ? 0.f : m_new;  // no key yet: no NaN
         // exponentials in place, summed in fp32 in four independent chains
         // (summing the bf16-rounded weights instead would put up to 2^-9
         // relative error into l when one weight dominates and the reference
@@ -307,12 +324,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         l_new = (rs[0] + rs[1]) + (rs[2] + rs[3]);  // taken against m_new
     };
     // Bring the old sums (u, and l before this half) to the new maximum, then
-    // add this half's sum.  alpha is the log2 factor m_old - m_new, 0 on lanes
-    // whose maximum did not move, so the exponential and the multiplies run
-    // only when some lane moved.
-    auto rescale = [&](float alpha, bool upd) {
+    // add this half's sum.  The log2 factor m_old - m_new is 0 on lanes whose
+    // maximum did not move, and the exponential and the multiplies run only
+    // when some lane moved.
+    auto rescale = [&](float m_use, bool upd) {
         if (__any(upd)) {
-            const float f = exp2_fast(alpha);
+            const float f = exp2_fast(m_run - m_use);
+            m_run = upd ? m_use : m_run;
+            m_thr = m_run + kLazyRescale;
 #pragma unroll
             for (int e = 0; e < T::DB; ++e) acc[e] *= f;
             l_run *= f;
@@ -346,11 +365,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     //      DO_S, P.V of the previous half (2*DB MFMAs, rows 32*vh of vs, with
     //      pb_prev) if DO_PV, and the softmax of s_cur into pb_new if DO_SM.
     //      MFMAs alternate S / P.V (independent neighbours) and every operand
-    //      is requested from LDS four MFMAs ahead; the compiler interleaves
+    //      is requested from LDS six MFMAs ahead; the compiler interleaves
     //      the softmax VALU work (pinning a fixed pattern measured slower). --
-    auto half_step = [&](auto do_s, auto do_pv, auto do_sm, int hsm, const bf16* ks, int kh,
-                         const bf16* vs, int vh, f32x16& s_cur, f32x16& s_nxt,
-                         const bf16x8 (&pb_prev)[2], bf16x8 (&pb_new)[2], float& alpha,
+    auto half_step = [&](auto do_s, auto do_pv, auto do_sm, auto chk, int hsm, const bf16* ks,
+                         int kh, const bf16* vs, int vh, f32x16& s_cur, f32x16& s_nxt,
+                         const bf16x8 (&pb_prev)[2], bf16x8 (&pb_new)[2], float& m_use,
                          bool& upd) {
         constexpr bool DO_S = decltype(do_s)::value, DO_PV = decltype(do_pv)::value;
         constexpr bool DO_SM = decltype(do_sm)::value;
@@ -376,7 +395,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         bf16x8 op[NM > 0 ? NM : 1];
 #pragma unroll
         for (int i = 0; i < PF && i < NM; ++i) op[i] = fetch(i);
-        if constexpr (DO_SM) softmax(s_cur, pb_new, alpha, upd, hsm);
+        if constexpr (DO_SM) softmax(s_cur, pb_new, m_use, upd, hsm, chk);
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
             if (i + PF < NM) op[i + PF] = fetch(i + PF);
@@ -405,14 +424,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         barrier_only();
         f32x16 sA, sB;  // scores of even / odd halves
         bf16x8 pA[2], pB[2];  // weights of even / odd halves
-        float alpha;
+        float m_use;  // reference maximum of the latest half's weights
         bool upd;
         sA = f32x16{};
     #pragma unroll
         for (int ss = 0; ss < T::DS; ++ss) sA = mfma32<E>(k_op(k_lds0, 0, ss), qreg[ss], sA);
         if (needs_mask(0)) apply_mask(sA, 0);
-        half_step(True{}, False{}, True{}, 0, k_lds0, 1, nullptr, 0, sA, sB, pB, pA, alpha, upd);
-        l_run = l_new;  // first half: nothing to rescale
+        half_step(True{}, False{}, True{}, True{}, 0, k_lds0, 1, nullptr, 0, sA, sB, pB, pA,
+                  m_use, upd);
+        m_run = upd ? m_use : m_run;  // first half: nothing to rescale
+        m_thr = m_run + kLazyRescale;
+        l_run = l_new;
         __syncthreads();  // K_0 is consumed before tile-step 0 reloads its buffer
 
         // ---- tile-steps.  Tile-step j runs half-steps 2j+1 (odd: softmax sB ->
@@ -426,20 +448,23 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         // flight while the reads proceed.
         // MASKED: the tile-step may hold halves on the causal diagonal or past
         // the end; interior tile-steps skip the checks, so their body holds
-        // no branch besides the (rare) rescale
+        // no branch besides the (rare) rescale.  Interior tile-steps only run
+        // when every row of the tile reads keys 0..95 (see j_int below), so
+        // half 0 already gave each row a finite maximum: their softmax needs
+        // no -inf guard (mask_tag doubles as CHK)
         auto tile_step = [&](int j, const bf16* __restrict__ k_rd, const bf16* __restrict__ v_rd,
                              bf16* __restrict__ k_wr, bf16* __restrict__ v_wr, auto mask_tag) {
             constexpr bool MASKED = decltype(mask_tag)::value;
             if (j + 2 < nkt) load_k((j + 2) * T::BC, k_wr);
             load_v((j + 1) * T::BC, v_wr);
             if (MASKED && needs_mask(2 * j + 1)) apply_mask(sB, 2 * j + 1);
-            half_step(True{}, True{}, True{}, 2 * j + 1, k_rd, 0, v_rd, 0, sB, sA, pA, pB, alpha,
-                      upd);
-            rescale(alpha, upd);
+            half_step(True{}, True{}, True{}, mask_tag, 2 * j + 1, k_rd, 0, v_rd, 0, sB, sA, pA,
+                      pB, m_use, upd);
+            rescale(m_use, upd);
             if (MASKED && needs_mask(2 * j + 2)) apply_mask(sA, 2 * j + 2);
-            half_step(True{}, True{}, True{}, 2 * j + 2, k_rd, 1, v_rd, 1, sA, sB, pB, pA, alpha,
-                      upd);
-            rescale(alpha, upd);
+            half_step(True{}, True{}, True{}, mask_tag, 2 * j + 2, k_rd, 1, v_rd, 1, sA, sB, pB,
+                      pA, m_use, upd);
+            rescale(m_use, upd);
             wait_vmem();  // K_{j+2} and V_{j+1} landed
             barrier_only();
         };
@@ -472,11 +497,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
             const int j = nkt - 1;
             const bf16* v_rd = (j & 1) ? v_lds1 : v_lds0;
             if (needs_mask(2 * j + 1)) apply_mask(sB, 2 * j + 1);
-            half_step(False{}, True{}, True{}, 2 * j + 1, nullptr, 0, v_rd, 0, sB, sA, pA, pB,
-                      alpha, upd);
-            rescale(alpha, upd);
-            half_step(False{}, True{}, False{}, 0, nullptr, 0, v_rd, 1, sA, sB, pB, pA, alpha,
-                      upd);
+            half_step(False{}, True{}, True{}, True{}, 2 * j + 1, nullptr, 0, v_rd, 0, sB, sA, pA,
+                      pB, m_use, upd);
+            rescale(m_use, upd);
+            half_step(False{}, True{}, False{}, True{}, 0, nullptr, 0, v_rd, 1, sA, sB, pB, pA,
+                      m_use, upd);
         }
         __syncthreads();  // LDS reads done before the next tile of the unit reloads
     }
