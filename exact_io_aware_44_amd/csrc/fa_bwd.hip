@@ -426,6 +426,18 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
             const int diag_end = min(nqt, qt_begin + 2);
             for (; qt < diag_end; ++qt) run_stage(qt, qt_begin, nqt, True{});
         }
+        // two interior stages per trip, so each reads and fills statically
+        // known LDS buffers and its operand addresses are a per-lane offset
+        // plus a constant (the stage parity is even here: 0 or 2 diagonal
+        // stages ran); the dropout kernel keeps one stage per trip, which
+        // fits its registers
+        if (!DROP && ((qt - qt_begin) & 1) == 0) {
+            for (; qt + 1 < nqt; qt += 2) {
+                step(qt, true, q_lds0, do_lds0, f_lds0, q_lds1, do_lds1, f_lds1, False{});
+                step(qt + 1, qt + 2 < nqt, q_lds1, do_lds1, f_lds1, q_lds0, do_lds0, f_lds0,
+                     False{});
+            }
+        }
         for (; qt < nqt; ++qt) run_stage(qt, qt_begin, nqt, False{});
 #pragma unroll
         for (int e = 0; e < T::DB; ++e) mfma_acc_drain(dv[e], dk[e]);
