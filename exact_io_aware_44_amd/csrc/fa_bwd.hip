@@ -129,8 +129,8 @@ __device__ __forceinline__ int qd_off(int r, int chunk) {  // element offset
 }
 
 // acc += A * B on v_mfma_f32_32x32x16_bf16 with acc held in AGPRs (the
-// compiler would otherwise keep it in VGPRs, which this kernel needs for K, V
-// and the score tiles).  Hazards the compiler cannot see through the asm:
+// compiler would otherwise keep it in VGPRs, which the dK/dV kernel needs for
+// K, V and the score tiles).  Hazards the compiler cannot see through the asm:
 //  - a VALU write of a or b needs two wait states before the MFMA reads it:
 //    the s_nop 1;
 //  - back-to-back accumulation into the same registers is interlocked;
@@ -459,10 +459,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // 3. dQ: unit = (batch, head, 128-query tile); wave w owns queries
-//    32w..32w+31 of the tile and keeps them (Q, dO as B operands) in VGPRs
-//    and their dQ^T accumulator in AGPRs while 64-key stages of K and V
-//    stream through double-buffered LDS.  Scores are taken transposed,
-//    S^T = K Q^T, so each lane holds one query and its L and D are scalars.
+//    32w..32w+31 of the tile and keeps them (Q, dO as B operands) and their
+//    dQ^T accumulator in VGPRs while 64-key stages of K and V stream through
+//    double-buffered LDS.  Scores are taken transposed, S^T = K Q^T, so each
+//    lane holds one query and its L and D are scalars.  Using no AGPRs
+//    leaves the kernel the whole 256-register budget of two waves per SIMD
+//    as VGPRs (any AGPR use splits that budget in half).
 // ---------------------------------------------------------------------------
 template <int D>
 struct QTile {
@@ -582,7 +584,7 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
                 const int cc = 4 * e + 2 * (g & 1) + ((i16 & 3) >> 1);
                 const int o0 = qd_off<D>(rr, cc) + 4 * (i16 & 1);
                 const int o1 = qd_off<D>(rr + 8, cc) + 4 * (i16 & 1);
-                mfma_acc<E>(acc[e], cat(lds_read_tr(ks + o0), lds_read_tr(ks + o1)), sb[t]);
+                acc[e] = mfma32<E>(cat(lds_read_tr(ks + o0), lds_read_tr(ks + o1)), sb[t], acc[e]);
             }
     };
     using True = std::true_type;
@@ -663,8 +665,6 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
         if (CAUSAL)
             for (; ks_i < nks; ++ks_i) run_stage(ks_i, nks, qw0, True{});
 
-#pragma unroll
-        for (int e = 0; e < T::DB; e += 2) mfma_acc_drain(acc[e], acc[e + 1]);
         // dQ[qi][d] = scale * acc (d = 32e + 8(r/4) + 4hi + r%4)
 #pragma unroll
         for (int e = 0; e < T::DB; ++e)
