@@ -116,6 +116,35 @@ def _check(t, name, shape=None, dtype=None):
                                                          tuple(shape)))
 
 
+def _check_lse(lse, shape, device):
+    """A caller-supplied L buffer: contiguous float32 of ``shape`` on the
+    GPU of q (a host tensor would hand the kernels a host address)."""
+    torch = _torch()
+    if lse is None:
+        return
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != tuple(shape)
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32 %s" % (list(shape),))
+    if not lse.is_cuda or lse.device != device:
+        raise ValueError("lse must be on %s like q" % (device,))
+
+
+def _check_workspace(ws, device):
+    """A caller-supplied workspace: contiguous, on the GPU of q."""
+    if ws is None:
+        return
+    if not ws.is_cuda or ws.device != device:
+        raise ValueError("workspace must be a GPU tensor on %s like q" % (device,))
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
+def _same_device(q, *named):
+    for t, name in named:
+        if t.device != q.device:
+            raise ValueError("%s is on %s, q on %s" % (name, t.device, q.device))
+
+
 def _fn(name, q):
     """The entry point for q's element type (the _f16 twin for float16)."""
     return getattr(load(), name + ("_f16" if q.dtype == _torch().float16 else ""))
@@ -153,11 +182,10 @@ def fa_fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None,
     _check(v, "v", q.shape, q.dtype)
     o = torch.empty_like(q) if out is None else out
     _check(o, "out", q.shape, q.dtype)
+    _same_device(q, (k, "k"), (v, "v"), (o, "out"))
     if lse is None and return_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)
-                            or not lse.is_contiguous()):
-        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    _check_lse(lse, (B, H, N), q.device)
     if dropout_p:
         rc = _fn("fa_fwd_dropout", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N,
                                       D, _scale(softmax_scale, D), int(bool(causal)),
@@ -189,11 +217,10 @@ def fa_fwd_qk(q, k, v, softmax_scale=None, causal=False, out=None, lse=None,
     _check(v, "v", (B, H, Nk, D), q.dtype)
     o = torch.empty_like(q) if out is None else out
     _check(o, "out", q.shape, q.dtype)
+    _same_device(q, (k, "k"), (v, "v"), (o, "out"))
     if lse is None and return_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq)
-                            or not lse.is_contiguous()):
-        raise ValueError("lse must be contiguous float32 [B, H, Nq]")
+    _check_lse(lse, (B, H, Nq), q.device)
     rc = _fn("fa_fwd_qk", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk,
                           D, _scale(softmax_scale, D), int(bool(causal)), _stream(stream))
     if rc != 0:
@@ -224,14 +251,14 @@ def fa_fwd_splitkv(q, k, v, softmax_scale=None, causal=False, num_splits=0, out=
     _check(v, "v", (B, H, Nk, D), q.dtype)
     o = torch.empty_like(q) if out is None else out
     _check(o, "out", q.shape, q.dtype)
+    _same_device(q, (k, "k"), (v, "v"), (o, "out"))
     if lse is None and return_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq)
-                            or not lse.is_contiguous()):
-        raise ValueError("lse must be contiguous float32 [B, H, Nq]")
+    _check_lse(lse, (B, H, Nq), q.device)
     need = fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = _fn("fa_fwd_splitkv", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                _ptr(workspace), ws_bytes, B, H, Nq, Nk, D,
@@ -256,11 +283,15 @@ def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None,
     _check(v, "v", q.shape, q.dtype)
     if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
         raise ValueError("cu_seqlens must be a 1-D int32 GPU tensor")
+    if not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be contiguous")
     nseq = cu_seqlens.shape[0] - 1
     o = torch.empty_like(q) if out is None else out
     _check(o, "out", q.shape, q.dtype)
+    _same_device(q, (k, "k"), (v, "v"), (o, "out"), (cu_seqlens, "cu_seqlens"))
     if lse is None and return_lse:
         lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    _check_lse(lse, (H, total), q.device)
     rc = _fn("fa_fwd_varlen", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                               _ptr(cu_seqlens), nseq, total, int(max_seqlen), H, D,
                               _scale(softmax_scale, D), int(bool(causal)),
@@ -283,16 +314,20 @@ def fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None,
     for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
         _check(t, name, q.shape, q.dtype)
     B, H, N, D = q.shape
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    if lse is None:
+        raise ValueError("lse from fa_fwd is required")
+    _check_lse(lse, (B, H, N), q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         _check(t, name, q.shape, q.dtype)
+    _same_device(q, (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"),
+                 (dv, "dv"))
     ws_bytes = fa_bwd_workspace_size(B, H, N, D)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q.device)
     if dropout_p:
         rc = _fn("fa_bwd_dropout", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                       _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
