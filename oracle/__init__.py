@@ -234,6 +234,31 @@ def bwd(q, k, v, dout, scale: float, causal: bool):
     return dq, dk, dv
 
 
+def bwd_varlen(q, k, v, dout, cu_seqlens, scale: float, causal: bool):
+    """Packed backward: gradients of <dout, O> for the packed forward
+    (``fwd_varlen``).  q, k, v, dout: [H, total, D]; cu_seqlens int [nseq+1].
+
+    The packed forward applies the plain definition inside each segment
+    [cu[b], cu[b+1]) and reads nothing outside it, so its Jacobian is block
+    diagonal over the segments: each segment's gradients are the dense
+    gradients (``bwd``) of that segment alone.  Tokens of no segment get
+    zero gradients.  Returns (dQ, dK, dV), each [H, total, D].
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    H, total, D = q.shape
+    cu = _i32(cu_seqlens)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(q), np.zeros_like(q)
+    for b in range(cu.shape[0] - 1):
+        s, e = int(cu[b]), int(cu[b + 1])
+        if e <= s:
+            continue
+        seg = [x[None, :, s:e] for x in (q, k, v, dout)]
+        g = bwd(*seg, scale, causal)
+        for out, gi in zip((dq, dk, dv), g):
+            out[:, s:e] = gi[0]
+    return dq, dk, dv
+
+
 def _i32(x) -> np.ndarray:
     if hasattr(x, "detach"):
         x = x.detach().cpu().numpy()
