@@ -15,7 +15,7 @@ import math
 import os
 
 __all__ = ["load", "build", "FaError", "fa_fwd", "fa_fwd_qk", "fa_fwd_splitkv",
-           "fa_fwd_splitkv_workspace_size", "fa_fwd_varlen", "fa_bwd",
+           "fa_fwd_splitkv_workspace_size", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen",
            "fa_bwd_workspace_size", "fa_status_string", "LIB_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +66,9 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            ctypes.c_size_t, _i, _i, _i, _i, _f, _i, _vp]
     lib.fa_bwd.restype = _i
+    lib.fa_bwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
+                                  _i, _vp, ctypes.c_size_t, _i, _i, _f, _i, _vp]
+    lib.fa_bwd_varlen.restype = _i
     lib.fa_status_string.argtypes = [_i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _u64 = ctypes.c_uint64
@@ -77,7 +80,7 @@ def load() -> ctypes.CDLL:
                                    _vp]
     lib.fa_bwd_dropout.restype = _i
     for name in ("fa_fwd", "fa_fwd_qk", "fa_fwd_splitkv", "fa_fwd_varlen", "fa_bwd",
-                 "fa_fwd_dropout", "fa_bwd_dropout"):
+                 "fa_bwd_varlen", "fa_fwd_dropout", "fa_bwd_dropout"):
         f16 = getattr(lib, name + "_f16")  # the fp16 twin: same arguments
         f16.argtypes = getattr(lib, name).argtypes
         f16.restype = _i
@@ -344,4 +347,48 @@ def fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None,
                               _scale(softmax_scale, D), int(bool(causal)), _stream(stream))
     if rc != 0:
         raise FaError(rc, "fa_bwd")
+    return dq, dk, dv
+
+
+def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, softmax_scale=None,
+                  causal=False, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward pass of fa_fwd_varlen.  q, k, v, o, dout: bf16 or fp16
+    [H, total, D]; lse: fp32 [H, total] from fa_fwd_varlen on the same
+    inputs; cu_seqlens: int32 GPU tensor [nseq + 1]; max_seqlen: host int >=
+    the longest sequence.
+
+    Returns (dq, dk, dv) [H, total, D] in q's element type.  ``workspace``
+    (GPU tensor of at least fa_bwd_workspace_size(1, H, total, D) bytes) is
+    allocated when not given.
+    """
+    torch = _torch()
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check(t, name, q.shape, q.dtype)
+    H, total, D = q.shape
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 GPU tensor")
+    if not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be contiguous")
+    nseq = cu_seqlens.shape[0] - 1
+    if lse is None:
+        raise ValueError("lse from fa_fwd_varlen is required")
+    _check_lse(lse, (H, total), q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, name, q.shape, q.dtype)
+    _same_device(q, (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"),
+                 (dv, "dv"), (cu_seqlens, "cu_seqlens"))
+    ws_bytes = fa_bwd_workspace_size(1, H, total, D)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q.device)
+    rc = _fn("fa_bwd_varlen", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), nseq, total,
+                                 int(max_seqlen), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), H, D,
+                                 _scale(softmax_scale, D), int(bool(causal)), _stream(stream))
+    if rc != 0:
+        raise FaError(rc, "fa_bwd_varlen")
     return dq, dk, dv

@@ -192,6 +192,33 @@ int bwd_impl(bool f16, const void* q, const void* k, const void* v, const void* 
     return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+int bwd_varlen_impl(bool f16, const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    const int32_t* cu_seqlens, int nseq, int total, int max_seqlen,
+                    void* workspace, size_t ws_bytes, int H, int D, float softmax_scale,
+                    int causal, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !cu_seqlens)
+        return FA_ERR_NULL;
+    if (nseq < 1 || total < 1 || max_seqlen < 1 || nseq > 65535) return FA_ERR_SHAPE;
+    if (int rc = check_common(H, D, softmax_scale, causal)) return rc;
+    if (H > 65535) return FA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+        !aligned16(dv) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+        return FA_ERR_ALIGN;
+    if (int rc = check_slice(total, D)) return rc;
+    // the workspace holds one row per packed token of every head
+    if (!workspace || ws_bytes < workspace_bytes(1, H, total)) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    if (max_seqlen > total) max_seqlen = total;  // no sequence is longer than total
+    fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace),
+                  nseq, H, total, D, softmax_scale, causal != 0};
+    a.f16 = f16;
+    a.cu = cu_seqlens;
+    a.max_seqlen = max_seqlen;
+    return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -290,6 +317,25 @@ int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o, const
                hipStream_t stream) {
     return bwd_impl(true, q, k, v, o, lse, dout, dq, dk, dv, workspace, ws_bytes, B, H, N,
                     D, softmax_scale, causal, stream);
+}
+
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                  const int32_t* cu_seqlens, int nseq, int total, int max_seqlen,
+                  void* workspace, size_t ws_bytes, int H, int D, float softmax_scale,
+                  int causal, hipStream_t stream) {
+    return bwd_varlen_impl(false, q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, nseq, total,
+                           max_seqlen, workspace, ws_bytes, H, D, softmax_scale, causal,
+                           stream);
+}
+int fa_bwd_varlen_f16(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      const int32_t* cu_seqlens, int nseq, int total, int max_seqlen,
+                      void* workspace, size_t ws_bytes, int H, int D, float softmax_scale,
+                      int causal, hipStream_t stream) {
+    return bwd_varlen_impl(true, q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, nseq, total,
+                           max_seqlen, workspace, ws_bytes, H, D, softmax_scale, causal,
+                           stream);
 }
 
 #define FA_DROPOUT_ENTRIES(SUFFIX, F16)                                                   \

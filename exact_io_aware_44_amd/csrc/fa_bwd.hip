@@ -51,7 +51,8 @@ struct BwdParams {
     bf16* dv;
     float* dd;     // [B, H, N]  D_i = dO_i . O_i
     float* nl2;    // [B, H, N]  -L_i * log2(e)
-    int H, N;
+    const int32_t* cu;  // packed sequences: offsets [nseq + 1] (varlen only)
+    int H, N;      // N: tokens per sequence (dense) or packed total (varlen)
     int per_head;  // dK/dV units per (batch, head): key tiles, or pairs if causal
     float c;       // scale * log2(e)
     float scale;
@@ -63,6 +64,27 @@ __device__ __forceinline__ void load4_lds(Buf b, uint32_t off, void* lds_wave_ba
     __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (FA_LDS void*)lds_wave_base, 4, off, 0,
                                              0, 0);
 }
+// Rows of the (batch, head) slice a unit works on.  Dense: N rows from
+// head * N.  Packed (varlen, [H, total, D], batch = sequence): the rows of
+// sequence b = head / H in head h's plane, [cu[b], cu[b+1]) clamped to
+// [0, total]; positions, and so the causal mask, count from the sequence
+// start and no key outside it is read.
+template <bool VARLEN>
+__device__ __forceinline__ void slice_rows(const BwdParams& p, int head, int& n,
+                                           int64_t& row0) {
+    if constexpr (VARLEN) {
+        const int b = head / p.H, h = head - b * p.H;
+        int s = p.cu[b], e = p.cu[b + 1];
+        s = min(max(s, 0), p.N);
+        e = min(max(e, s), p.N);
+        n = e - s;
+        row0 = (int64_t)h * p.N + s;
+    } else {
+        n = p.N;
+        row0 = (int64_t)head * p.N;
+    }
+}
+
 // s_waitcnt vmcnt(0) lgkmcnt(0): this wave's loads (global and LDS) are done.
 __device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0070); }
 
@@ -148,7 +170,7 @@ __device__ __forceinline__ void mfma_acc_drain(f32x16& a, f32x16& b) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(a), "+a"(b));
 }
 
-template <typename E, int D, bool CAUSAL, bool DROP>
+template <typename E, int D, bool CAUSAL, bool DROP, bool VARLEN>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     using T = KvTile<D>;
     // one LDS object per buffer, selected statically, so the compiler can tell
@@ -166,14 +188,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     const int g = lane >> 4, i16 = lane & 15;
     int head, uidx;
     unit_of(blockIdx.x, gridDim.x, p.per_head, head, uidx);
-    const int n = p.N;
+    int n;
+    int64_t row0;
+    slice_rows<VARLEN>(p, head, n, row0);
     const int nkt = (n + T::BK - 1) / T::BK;
     // key tiles of this unit: under causal masking a heavy one (many queries
     // follow it) and the matching light one, so all units carry equal work
     int kt0, kt1;
     if (!unit_tiles(CAUSAL, false, uidx, nkt, kt0, kt1)) return;
 
-    const int64_t row0 = (int64_t)head * n;
     const uint32_t bytes = (uint32_t)n * D * 2;
     const Buf qb = make_buf(p.q + row0 * D, bytes);
     const Buf kb = make_buf(p.k + row0 * D, bytes);
@@ -479,7 +502,7 @@ struct QTile {
     static constexpr int DB = D / 32;
 };
 
-template <typename E, int D, bool CAUSAL, bool DROP>
+template <typename E, int D, bool CAUSAL, bool DROP, bool VARLEN>
 __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
     using T = QTile<D>;
     __shared__ __attribute__((aligned(16))) bf16 k_lds0[T::T_ELEMS];
@@ -493,14 +516,15 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
     const int g = lane >> 4, i16 = lane & 15;
     int head, uidx;
     unit_of(blockIdx.x, gridDim.x, p.per_head, head, uidx);
-    const int n = p.N;
+    int n;
+    int64_t row0;
+    slice_rows<VARLEN>(p, head, n, row0);
     const int nqt = (n + T::BR - 1) / T::BR;
     // query tiles of this unit: under causal masking a heavy one (late, many
     // keys) and the matching light one
     int t0, t1;
     if (!unit_tiles(CAUSAL, true, uidx, nqt, t0, t1)) return;
 
-    const int64_t row0 = (int64_t)head * n;
     const uint32_t bytes = (uint32_t)n * D * 2;
     const Buf qb = make_buf(p.q + row0 * D, bytes);
     const Buf kb = make_buf(p.k + row0 * D, bytes);
@@ -678,7 +702,7 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
     }
 }
 
-template <typename E, int D, bool CAUSAL, bool DROP>
+template <typename E, int D, bool CAUSAL, bool DROP, bool VARLEN = false>
 hipError_t run_bwd(const BwdArgs& a, hipStream_t stream) {
     BwdParams p;
     p.q = static_cast<const bf16*>(a.q);
@@ -690,9 +714,11 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream) {
     p.dq = static_cast<bf16*>(a.dq);
     p.dk = static_cast<bf16*>(a.dk);
     p.dv = static_cast<bf16*>(a.dv);
-    const int64_t rows = (int64_t)a.B * a.H * a.N;
+    // rows of [B, H, N] (dense) or of [H, total] (varlen: N = total)
+    const int64_t rows = VARLEN ? (int64_t)a.H * a.N : (int64_t)a.B * a.H * a.N;
     p.dd = a.ws;
     p.nl2 = a.ws + ((rows + 63) & ~(int64_t)63);  // second region, 256-byte aligned
+    p.cu = a.cu;
     p.H = a.H;
     p.N = a.N;
     p.c = (float)((double)a.scale * 1.4426950408889634);
@@ -705,25 +731,37 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
 
-    const int nkt = (a.N + KvTile<D>::BK - 1) / KvTile<D>::BK;
+    // units per (sequence, head) come from the longest sequence; units past
+    // a shorter sequence's tiles return at once
+    const int nmax = VARLEN ? a.max_seqlen : a.N;
+    const int nkt = (nmax + KvTile<D>::BK - 1) / KvTile<D>::BK;
     p.per_head = CAUSAL ? (nkt + 1) / 2 : nkt;
     const int64_t units = (int64_t)p.per_head * a.H * a.B;
-    hipLaunchKernelGGL((dkdv_kernel<E, D, CAUSAL, DROP>), dim3((unsigned)units), dim3(256), 0,
-                       stream, p);
+    hipLaunchKernelGGL((dkdv_kernel<E, D, CAUSAL, DROP, VARLEN>), dim3((unsigned)units),
+                       dim3(256), 0, stream, p);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
 
     // the dQ pass: per_head query tiles (pairs under causal masking)
-    const int nqt = (a.N + QTile<D>::BR - 1) / QTile<D>::BR;
+    const int nqt = (nmax + QTile<D>::BR - 1) / QTile<D>::BR;
     p.per_head = CAUSAL ? (nqt + 1) / 2 : nqt;
     const int64_t qunits = (int64_t)p.per_head * a.H * a.B;
-    hipLaunchKernelGGL((dq_kernel<E, D, CAUSAL, DROP>), dim3((unsigned)qunits), dim3(256), 0, stream,
-                       p);
+    hipLaunchKernelGGL((dq_kernel<E, D, CAUSAL, DROP, VARLEN>), dim3((unsigned)qunits),
+                       dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
 template <typename E, bool DROP>
 hipError_t run_bwd_d(const BwdArgs& a, hipStream_t stream) {
+    if constexpr (!DROP) {
+        if (a.cu) {  // packed sequences (no dropout on this path)
+            if (a.D == 64)
+                return a.causal ? run_bwd<E, 64, true, false, true>(a, stream)
+                                : run_bwd<E, 64, false, false, true>(a, stream);
+            return a.causal ? run_bwd<E, 128, true, false, true>(a, stream)
+                            : run_bwd<E, 128, false, false, true>(a, stream);
+        }
+    }
     if (a.D == 64)
         return a.causal ? run_bwd<E, 64, true, DROP>(a, stream)
                         : run_bwd<E, 64, false, DROP>(a, stream);

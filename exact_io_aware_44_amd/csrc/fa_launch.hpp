@@ -51,11 +51,13 @@ struct BwdArgs {
     void* dv;
     float* ws;              // workspace: two fp32 [B, H, N] regions, each
                             // padded to 256 bytes (D_i, then -L_i log2 e)
-    int B, H, N, D;
+    int B, H, N, D;         // varlen: B = number of sequences, N = packed total
     float scale;
     bool causal;
     bool f16 = false;       // element type: bf16, or fp16 when set
     Dropout drop{};         // thresh 0: no dropout
+    const int32_t* cu = nullptr;  // packed offsets [B + 1] (varlen) or null (dense)
+    int max_seqlen = 0;     // longest sequence (varlen)
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);

@@ -204,6 +204,40 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            float softmax_scale, int causal, hipStream_t stream);
 
 /*
+ * Backward pass over packed variable-length sequences: the gradients of
+ * fa_fwd_varlen, computed as fa_bwd computes them for each sequence on its
+ * own (tensortonic section 7 for the recomputation; the causal mask and the
+ * sequence bounds are those of fa_fwd_varlen, so no gradient flows between
+ * sequences).  There is no dropout.
+ *
+ *   q, k, v, o, dout   in   bf16 [H, total, D], tokens packed along the token
+ *                           axis as for fa_fwd_varlen; o and lse must come
+ *                           from fa_fwd_varlen on the same q, k, v,
+ *                           cu_seqlens, scale and causal
+ *   lse                in   fp32 [H, total]
+ *   dq, dk, dv         out  bf16 [H, total, D] (rows of every sequence
+ *                           overwritten)
+ *   cu_seqlens         in   DEVICE int32 [nseq + 1] with the contract of
+ *                           fa_fwd_varlen (clamped to [0, total] in the
+ *                           kernels, so malformed offsets never cause
+ *                           out-of-range accesses)
+ *   max_seqlen         host int >= every sequence length (sizes the grid;
+ *                           rows of a longer sequence are not written)
+ *   nseq, total, max_seqlen, H >= 1;  D in {64, 128}
+ *   workspace          scratch device memory of at least
+ *                      fa_bwd_workspace_size(1, H, total, D) bytes (one row
+ *                      per packed token and head); contents on entry are
+ *                      ignored, on exit unspecified
+ *
+ * Status codes are those of fa_fwd_varlen and fa_bwd.
+ */
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                  const int32_t* cu_seqlens, int nseq, int total, int max_seqlen,
+                  void* workspace, size_t workspace_bytes, int H, int D,
+                  float softmax_scale, int causal, hipStream_t stream);
+
+/*
  * Attention dropout (tensortonic section 7: with dropout enabled the
  * backward pass must reproduce the forward pass's drop decisions from saved
  * generator state, never draw a new mask).  After the softmax each weight
@@ -247,6 +281,11 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
  */
 int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                int H, int N, int D, float softmax_scale, int causal, hipStream_t stream);
+int fa_bwd_varlen_f16(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      const int32_t* cu_seqlens, int nseq, int total, int max_seqlen,
+                      void* workspace, size_t workspace_bytes, int H, int D,
+                      float softmax_scale, int causal, hipStream_t stream);
 int fa_fwd_qk_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                   int H, int Nq, int Nk, int D, float softmax_scale, int causal,
                   hipStream_t stream);

@@ -36,6 +36,7 @@ def _declared():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert names == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_dropout_f16", "fa_bwd_f16",
+                     "fa_bwd_varlen", "fa_bwd_varlen_f16",
                      "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_dropout",
                      "fa_fwd_dropout_f16", "fa_fwd_f16", "fa_fwd_qk", "fa_fwd_qk_f16",
                      "fa_fwd_splitkv",
@@ -186,6 +187,34 @@ def bwd(lib, q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, ws=P,
 ])
 def test_bwd_rejects(lib, kw, code):
     assert bwd(lib, **kw) == code
+
+
+def bwd_varlen(lib, q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, cu=P, nseq=2,
+               total=32, maxlen=16, ws=P, ws_bytes=1 << 20, H=2, D=128, scale=0.1,
+               causal=1):
+    return lib.fa_bwd_varlen(q, k, v, o, lse, do, dq, dk, dv, cu, nseq, total, maxlen, ws,
+                             ws_bytes, H, D, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(lse=None), NULL), (dict(do=None), NULL),
+    (dict(dv=None), NULL), (dict(cu=None), NULL),
+    (dict(nseq=0), SHAPE), (dict(total=0), SHAPE), (dict(maxlen=0), SHAPE),
+    (dict(H=0), SHAPE), (dict(nseq=70000), SHAPE),
+    (dict(D=32), UNSUP), (dict(causal=2), UNSUP), (dict(scale=float("nan")), ARG),
+    (dict(cu=P + 2), ALIGN), (dict(dq=PM), ALIGN), (dict(ws=PM), ALIGN),
+    (dict(ws=None), WS),
+    # one row per packed token and head: H * total fp32 values, twice
+    (dict(ws_bytes=2 * 2 * 32 * 4 - 1), WS),
+    (dict(total=1 << 23, D=128), TOO_LARGE),
+])
+def test_bwd_varlen_rejects(lib, kw, code):
+    assert bwd_varlen(lib, **kw) == code
+
+
+def test_bwd_varlen_workspace_is_dense_size_of_packed_rows(lib):
+    # fa_bwd_varlen takes fa_bwd_workspace_size(1, H, total, D) bytes
+    assert fa.fa_bwd_workspace_size(1, 2, 32, 128) == 2 * 2 * 32 * 4
 
 
 def test_python_binding_checks_dtypes():
