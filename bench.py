@@ -8,7 +8,8 @@ the forward kernel, the backward pass (fa_bwd, B2 H32 N4096 D128 causal)
 against the same roofline, the decoding-shaped forward (fa_fwd_splitkv, one
 query against a 16384-token cache, B8 H32 D128) against HBM bandwidth, the
 varlen (16 packed causal sequences) and long-context (B1 H32 N65536)
-forwards, the metric workload with L2/MALL flushed before each launch, and
+forwards, the varlen backward (fa_bwd_varlen), the metric workload with
+L2/MALL flushed before each launch, and
 the fp64 CPU oracle timed on a bounded sample of the same workload.
 
 FLOP convention: 4*D flops per (query, key) pair, causal counted as half of
@@ -185,7 +186,8 @@ def gpu_randn_bf16(torch, shape, seed):
 
 
 def run_other_configs(torch, ai, fa, steps):
-    """The varlen and long-context forward workloads, same roofline."""
+    """The varlen forward and backward and the long-context forward
+    workloads, same roofline."""
     out = {}
     # varlen: 16 causal sequences, lengths U[128, 8192], packed [H, total, D]
     lengths = ai.varlen_lengths(ai.VARLEN_LENGTH_SEED)
@@ -205,7 +207,21 @@ def run_other_configs(torch, ai, fa, steps):
     _, per = time_launches(torch, vstep, steps, 3)
     flops = sum(4.0 * H * D * n * n * 0.5 for n in lengths)
     out["varlen"] = launch_stats(ai.VARLEN_NAME, flops, per)
-    del q, k, v, o, lse
+    # the packed backward on the same workload (three launches per call;
+    # counted as 2.5x the forward's flops)
+    do = gpu_randn_bf16(torch, (H, total, D), ai.VARLEN_DATA_SEED * 10 + 3)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa.fa_bwd_workspace_size(1, H, total, D), dtype=torch.uint8,
+                     device="cuda")
+
+    def vbstep():
+        fa.fa_bwd_varlen(q, k, v, o, lse, do, cu, max(lengths), softmax_scale=scale,
+                         causal=True, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    _, per = time_launches(torch, vbstep, steps, 2)
+    out["varlen_backward"] = launch_stats("varlen causal bwd 16 seqs U[128,8192] H32 D128",
+                                          2.5 * flops, per)
+    del q, k, v, o, lse, do, dq, dk, dv, ws
     # long context: B1 H32 N65536 D128 causal
     w = ai.LONG
     log("long:", w.name)
@@ -351,6 +367,7 @@ def main(argv=None):
         "backward": backward,
         "decode": decode,
         "varlen": others.get("varlen"),
+        "varlen_backward": others.get("varlen_backward"),
         "long": others.get("long"),
     }
     if rank == 0 and args.cpu_budget > 0:

@@ -87,3 +87,24 @@ def test_fp16(gpu):
         e = rel_l2(g_, r)
         say("  fp16 %s rel-L2 %.3e" % (name, e))
         assert e <= GRAD_REL_L2, (name, e)
+
+
+def test_varlen_workload_full_size_sampled_heads(gpu):
+    """16 sequences with lengths ~ U[128, 8192] (seeded), H32 D128, causal,
+    all heads on the GPU; one seeded head against the oracle's exact
+    gradients, every sequence of that head (about 10 s of fp64 work)."""
+    q, k, v, cu, lengths = ai.varlen_inputs()
+    H, total, D = q.shape
+    say("case varlen bwd full size, total", total)
+    do = ai.randn_bf16((H, total, D), ai.generator(ai.VARLEN_DATA_SEED + 100))
+    scale = ai.default_scale(D)
+    got = _grads(gpu, q, k, v, do, cu, max(lengths), scale, True)
+    g = ai.generator(51)
+    heads = [int(x) for x in torch.randperm(H, generator=g)[:1]]
+    for h in heads:
+        sl = slice(h, h + 1)
+        refs = oracle.bwd_varlen(q[sl], k[sl], v[sl], do[sl], cu, scale, True)
+        for name, g_, r in zip(("dQ", "dK", "dV"), got, refs):
+            e = rel_l2(g_[sl], r)
+            say("  head %d %s rel-L2 %.3e" % (h, name, e))
+            assert e <= GRAD_REL_L2, (h, name, e)
