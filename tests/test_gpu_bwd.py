@@ -72,3 +72,19 @@ def test_backward_workload_sampled_heads(gpu):
         sl = (slice(b, b + 1), slice(h, h + 1))
         ref = oracle.bwd(q[sl], k[sl], v[sl], do[sl], w.scale, True)
         _check([x[sl] for x in got], ref, "%s b%d h%d" % (w.name, b, h))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_backward_sampled_head(gpu, causal):
+    """B1 H4 N8192 D128: many 64-query stages per key tile and 128-query
+    tiles per unit; one seeded head against the oracle's exact gradients."""
+    B, H, N, D = 1, 4, 8192, 128
+    say("case long bwd B%d H%d N%d D%d causal %d" % (B, H, N, D, causal))
+    q, k, v = ai.qkv(B, H, N, D, 70 + causal)
+    do = ai.randn_bf16((B, H, N, D), 72 + causal)
+    scale = ai.default_scale(D)
+    got = _fwd_bwd(gpu, q, k, v, do, scale, causal)
+    h = int(torch.randint(0, H, (1,), generator=ai.generator(73 + causal)))
+    sl = (slice(0, 1), slice(h, h + 1))
+    ref = oracle.bwd(q[sl], k[sl], v[sl], do[sl], scale, causal)
+    _check([x[sl] for x in got], ref, "long bwd h%d causal %d" % (h, causal))
