@@ -27,7 +27,7 @@
 //    branch-free block, the MFMAs of S_{h+1} = K_{h+1} Q^T and of
 //    O^T += V_{h-1}^T P_{h-1}^T together with the VALU softmax of S_h.  The
 //    three are independent, so the wave keeps the matrix pipe busy while its
-//    own exponentials run; every MFMA operand is requested from LDS four
+//    own exponentials run; every MFMA operand is requested from LDS six
 //    MFMAs ahead.  Two workgroups per CU give each SIMD a second such wave.
 //  - Exponentials use exp2 with scale*log2(e) folded into one FMA per score;
 //    the running maximum moves lazily (see kLazyRescale), so the accumulator
