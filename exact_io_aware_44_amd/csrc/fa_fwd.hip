@@ -512,21 +512,51 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     // kept weights carry 1 / (1 - p'), folded into the normalisation
     const float inv = l_tot > 0.f ? (DROP ? p.drop.inv_keep : 1.f) / l_tot : 0.f;
     const float L = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : kNegInf;
+    if constexpr (SPLIT) {
 #pragma unroll
-    for (int e = 0; e < T::DB; ++e)
+        for (int e = 0; e < T::DB; ++e)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int d = 32 * e + 8 * r4 + 4 * hi;
-            if constexpr (SPLIT) {
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = 32 * e + 8 * r4 + 4 * hi;
                 const f32x4 ov{acc[e][4 * r4] * inv, acc[e][4 * r4 + 1] * inv,
                                acc[e][4 * r4 + 2] * inv, acc[e][4 * r4 + 3] * inv};
                 store16(pob, ((uint32_t)qi * D + d) * 4, __builtin_bit_cast(u32x4, ov));
-            } else {
-                store8(ob, ((uint32_t)qi * D + d) * 2,
-                       pack4<E>(acc[e][4 * r4] * inv, acc[e][4 * r4 + 1] * inv,
-                             acc[e][4 * r4 + 2] * inv, acc[e][4 * r4 + 3] * inv));
             }
+    } else {
+        // O leaves through LDS: a lane holds 8-byte pieces of one row, and
+        // stored directly each store instruction would write 32 rows in
+        // 16-byte pieces.  The wave stages its 32 rows in a K buffer (free
+        // after the last tile-step) and writes them back as whole rows, 16
+        // bytes per lane.  Staged rows are padded by 16 bytes so the 8-byte
+        // writes of 32 rows spread over the banks.
+        constexpr int OSTR = D + 8;
+        constexpr int RPI = 64 / T::CPR;  // rows per read-back instruction
+        static_assert(2 * 32 * OSTR <= T::K_ELEMS, "two waves' rows fit in one K buffer");
+        bf16* const ost = ((wave & 2) ? k_lds1 : k_lds0) + (wave & 1) * 32 * OSTR;
+#pragma unroll
+        for (int e = 0; e < T::DB; ++e)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = 32 * e + 8 * r4 + 4 * hi;
+                *reinterpret_cast<u32x2*>(ost + l32 * OSTR + d) =
+                    pack4<E>(acc[e][4 * r4] * inv, acc[e][4 * r4 + 1] * inv,
+                             acc[e][4 * r4 + 2] * inv, acc[e][4 * r4 + 3] * inv);
+            }
+        // the wave reads rows other lanes wrote: its writes land first
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int t = 0; t < 32 / RPI; ++t) {
+            const int i = RPI * t + lane / T::CPR, c = lane % T::CPR;
+            const u32x4 w = *reinterpret_cast<const u32x4*>(ost + i * OSTR + 8 * c);
+            store16(ob, ((uint32_t)(q0 + 4 * i + wave) * D + 8 * c) * 2, w);
         }
+        // the next tile's loads refill the K buffers: every wave's reads first
+        if (rep + 1 < ntiles) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            barrier_only();
+        }
+    }
     if (hi == 0) store4(SPLIT ? plb : lb, (uint32_t)qi * 4, __builtin_bit_cast(uint32_t, L));
     }  // query tiles of the unit
 }
