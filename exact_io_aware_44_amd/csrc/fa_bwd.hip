@@ -88,6 +88,39 @@ __device__ __forceinline__ void slice_rows(const BwdParams& p, int head, int& n,
 // s_waitcnt vmcnt(0) lgkmcnt(0): this wave's loads (global and LDS) are done.
 __device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0070); }
 
+// Writes a wave's 32 rows of a transposed accumulator to rows base ..
+// base + 31 of dst, times `scale`.  In the accumulator a lane holds 8-byte
+// pieces of one row (lane: row l32, columns 32e + 8(r/4) + 4hi + r%4 of
+// acc[e], register r); stored directly, each store instruction would write 32
+// rows in 16-byte pieces.  The rows are staged in st (32 x (D + 8) elements,
+// this wave's own LDS region; the 16-byte row padding spreads the 8-byte
+// writes over the banks) and written back as whole rows, 16 bytes per lane.
+template <typename E, int D>
+__device__ __forceinline__ void store_rows(bf16* st, const f32x16* acc, float scale, Buf dst,
+                                           int base, int lane) {
+    constexpr int OSTR = D + 8, CPR = D / 8, RPI = 64 / CPR;
+    const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+    for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+            *reinterpret_cast<u32x2*>(st + l32 * OSTR + 32 * e + 8 * r4 + 4 * hi) =
+                pack4<E>(acc[e][4 * r4] * scale, acc[e][4 * r4 + 1] * scale,
+                         acc[e][4 * r4 + 2] * scale, acc[e][4 * r4 + 3] * scale);
+    // the wave reads rows other lanes wrote: its writes land first
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int t = 0; t < 32 / RPI; ++t) {
+        const int i = RPI * t + lane / CPR, c = lane % CPR;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(st + i * OSTR + 8 * c);
+        store16(dst, ((uint32_t)(base + i) * D + 8 * c) * 2, w);
+    }
+    // reads done before the region is written again
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+}
+
 // ---------------------------------------------------------------------------
 // 1. Per-row constants: D_i = dO_i . O_i (fp32 sum of exact bf16 products)
 //    and -L_i log2(e), the exponent offset that turns a score into its weight.
@@ -464,19 +497,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
         for (; qt < nqt; ++qt) run_stage(qt, qt_begin, nqt, False{});
 #pragma unroll
         for (int e = 0; e < T::DB; ++e) mfma_acc_drain(dv[e], dk[e]);
-        // dV[kj][d], dK[kj][d] = scale * acc (d = 32e + 8(r/4) + 4hi + r%4)
-#pragma unroll
-        for (int e = 0; e < T::DB; ++e)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int d = 32 * e + 8 * r4 + 4 * hi;
-                const uint32_t off = ((uint32_t)kj * D + d) * 2;
-                store8(dvb, off, pack4<E>(dv[e][4 * r4], dv[e][4 * r4 + 1],
-                                       dv[e][4 * r4 + 2], dv[e][4 * r4 + 3]));
-                store8(dkb, off,
-                       pack4<E>(dk[e][4 * r4] * p.scale, dk[e][4 * r4 + 1] * p.scale,
-                             dk[e][4 * r4 + 2] * p.scale, dk[e][4 * r4 + 3] * p.scale));
-            }
+        // dV[kj][d] = acc, dK[kj][d] = scale * acc, through a Q/dO stage
+        // buffer of this wave's own (all waves are past the last stage's
+        // barrier, so none reads them any more)
+        static_assert(32 * (D + 8) <= T::T_ELEMS, "a wave's rows fit in one stage buffer");
+        bf16* const st = wave == 0 ? q_lds0 : wave == 1 ? q_lds1 : wave == 2 ? do_lds0 : do_lds1;
+        store_rows<E, D>(st, dv, 1.f, dvb, kw0, lane);
+        store_rows<E, D>(st, dk, p.scale, dkb, kw0, lane);
+        // the second key tile's first stage refills these buffers
+        if (rep == 0 && kt1 >= 0) barrier_only();
     }
 }
 
@@ -689,16 +718,13 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
         if (CAUSAL)
             for (; ks_i < nks; ++ks_i) run_stage(ks_i, nks, qw0, True{});
 
-        // dQ[qi][d] = scale * acc (d = 32e + 8(r/4) + 4hi + r%4)
-#pragma unroll
-        for (int e = 0; e < T::DB; ++e)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int d = 32 * e + 8 * r4 + 4 * hi;
-                store8(dqb, ((uint32_t)qi * D + d) * 2,
-                       pack4<E>(acc[e][4 * r4] * p.scale, acc[e][4 * r4 + 1] * p.scale,
-                             acc[e][4 * r4 + 2] * p.scale, acc[e][4 * r4 + 3] * p.scale));
-            }
+        // dQ[qi][d] = scale * acc, through a K/V stage buffer of this
+        // wave's own (all waves are past the last stage's barrier)
+        static_assert(32 * (D + 8) <= T::T_ELEMS, "a wave's rows fit in one stage buffer");
+        bf16* const st = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
+        store_rows<E, D>(st, acc, p.scale, dqb, qw0, lane);
+        // the second query tile's first stage refills these buffers
+        if (rep == 0 && t1 >= 0) barrier_only();
     }
 }
 
