@@ -84,8 +84,11 @@ def _load():
     lib.oracle_attn_bwd_dropout.argtypes = [_D, _D, _D, _D, _D, _D, _D, _i64, _i64, _i64,
                                             _i64, ctypes.c_double, ctypes.c_int,
                                             ctypes.c_double, _u64, _u64]
+    lib.oracle_attn_fwd_dropout_bh.argtypes = lib.oracle_attn_fwd_dropout.argtypes + [_i64]
+    lib.oracle_attn_bwd_dropout_bh.argtypes = lib.oracle_attn_bwd_dropout.argtypes + [_i64]
     for f in (lib.oracle_dropout_mask, lib.oracle_attn_fwd_dropout,
-              lib.oracle_attn_bwd_dropout):
+              lib.oracle_attn_bwd_dropout, lib.oracle_attn_fwd_dropout_bh,
+              lib.oracle_attn_bwd_dropout_bh):
         f.restype = ctypes.c_int
     lib.oracle_attn_bwd.argtypes = [_D, _D, _D, _D, _D, _D, _D, _i64, _i64,
                                     _i64, _i64, ctypes.c_double, ctypes.c_int]
@@ -315,4 +318,56 @@ def bwd_dropout(q, k, v, dout, scale: float, causal: bool, p: float, seed: int,
                                            _p(dv), B, H, N, D, float(scale),
                                            int(bool(causal)), float(p), int(seed),
                                            int(offset)), "bwd_dropout")
+    return dq, dk, dv
+
+
+def _segments(cu_seqlens):
+    cu = _i32(cu_seqlens)
+    return [(b, int(cu[b]), int(cu[b + 1])) for b in range(cu.shape[0] - 1)
+            if int(cu[b + 1]) > int(cu[b])]
+
+
+def fwd_varlen_dropout(q, k, v, cu_seqlens, scale: float, causal: bool, p: float, seed: int,
+                       offset: int):
+    """Packed forward with attention dropout.  q, k, v: [H, total, D].
+
+    Each sequence b of each head h is the dense dropout forward (``fwd_dropout``'s
+    arithmetic) of that segment alone, its decisions drawn as head b * H + h with
+    positions counted from the sequence start.  Returns (O [H, total, D],
+    L [H, total]); tokens of no sequence get O = 0, L = -inf.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    H, total, D = q.shape
+    o = np.zeros_like(q)
+    lse = np.full((H, total), -np.inf)
+    for b, s, e in _segments(cu_seqlens):
+        for h in range(H):
+            qs, ks, vs = (np.ascontiguousarray(x[h, s:e]) for x in (q, k, v))
+            os_ = np.empty_like(qs)
+            ls = np.empty((e - s,), dtype=np.float64)
+            _check(_load().oracle_attn_fwd_dropout_bh(
+                _p(qs), _p(ks), _p(vs), _p(os_), _p(ls), 1, 1, e - s, D, float(scale),
+                int(bool(causal)), float(p), int(seed), int(offset), b * H + h),
+                "fwd_varlen_dropout")
+            o[h, s:e], lse[h, s:e] = os_, ls
+    return o, lse
+
+
+def bwd_varlen_dropout(q, k, v, dout, cu_seqlens, scale: float, causal: bool, p: float,
+                       seed: int, offset: int):
+    """Packed backward with attention dropout, the same decisions as
+    ``fwd_varlen_dropout``: per sequence and head, ``bwd_dropout``'s exact
+    gradients of that segment alone.  Returns (dQ, dK, dV), each [H, total, D]."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    H, total, D = q.shape
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(q), np.zeros_like(q)
+    for b, s, e in _segments(cu_seqlens):
+        for h in range(H):
+            qs, ks, vs, ds = (np.ascontiguousarray(x[h, s:e]) for x in (q, k, v, dout))
+            g = [np.empty_like(qs) for _ in range(3)]
+            _check(_load().oracle_attn_bwd_dropout_bh(
+                _p(qs), _p(ks), _p(vs), _p(ds), _p(g[0]), _p(g[1]), _p(g[2]), 1, 1, e - s,
+                D, float(scale), int(bool(causal)), float(p), int(seed), int(offset),
+                b * H + h), "bwd_varlen_dropout")
+            dq[h, s:e], dk[h, s:e], dv[h, s:e] = g
     return dq, dk, dv

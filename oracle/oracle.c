@@ -503,11 +503,13 @@ int oracle_dropout_mask(uint8_t* keep, int64_t bh, int64_t nq, int64_t nk, doubl
 }
 
 /* Dense forward with dropout: O_i = sum_j P_ij keep_ij / (1 - p') v_j;
- * L_i = m_i + ln l_i of the undropped scores. */
-int oracle_attn_fwd_dropout(const double* q, const double* k, const double* v, double* o,
-                            double* lse, int64_t B, int64_t H, int64_t N, int64_t D,
-                            double scale, int causal, double p, uint64_t seed,
-                            uint64_t offset) {
+ * L_i = m_i + ln l_i of the undropped scores.  Slice bh of the B*H slices
+ * draws its decisions as head bh_base + bh (0 for a whole batch; a packed
+ * sequence b passes b * H + h for its one head). */
+int oracle_attn_fwd_dropout_bh(const double* q, const double* k, const double* v, double* o,
+                               double* lse, int64_t B, int64_t H, int64_t N, int64_t D,
+                               double scale, int causal, double p, uint64_t seed,
+                               uint64_t offset, int64_t bh_base) {
     if (B < 0 || H < 0 || N < 0 || D <= 0 || !(p >= 0.0 && p < 1.0)) return 1;
     const int T = oracle_dropout_threshold(p);
     const double inv_keep = 256.0 / (256.0 - T);
@@ -537,7 +539,7 @@ int oracle_attn_fwd_dropout(const double* q, const double* k, const double* v, d
                     l += s[j];
                 }
                 for (int64_t j = 0; j < nk; ++j) {
-                    if (!keep_bit(seed, offset, bh, i, j, T)) continue;
+                    if (!keep_bit(seed, offset, bh_base + bh, i, j, T)) continue;
                     const double w = s[j] / l * inv_keep;
                     const double* v_j = v + base + j * D;
                     for (int64_t d = 0; d < D; ++d) o_i[d] += w * v_j[d];
@@ -558,10 +560,11 @@ int oracle_attn_fwd_dropout(const double* q, const double* k, const double* v, d
  *   dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik),
  *   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i.
  */
-int oracle_attn_bwd_dropout(const double* q, const double* k, const double* v,
-                            const double* dout, double* dq, double* dk, double* dv,
-                            int64_t B, int64_t H, int64_t N, int64_t D, double scale,
-                            int causal, double p, uint64_t seed, uint64_t offset) {
+int oracle_attn_bwd_dropout_bh(const double* q, const double* k, const double* v,
+                               const double* dout, double* dq, double* dk, double* dv,
+                               int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                               int causal, double p, uint64_t seed, uint64_t offset,
+                               int64_t bh_base) {
     if (B < 0 || H < 0 || N < 0 || D <= 0 || !(p >= 0.0 && p < 1.0)) return 1;
     if (N == 0) return 0;
     const int T = oracle_dropout_threshold(p);
@@ -605,7 +608,7 @@ int oracle_attn_bwd_dropout(const double* q, const double* k, const double* v,
                     for (int64_t j = 0; j < nk; ++j) {
                         pr[j] /= l;
                         const double z =
-                            keep_bit(seed, offset, bh, i, j, T) ? inv_keep : 0.0;
+                            keep_bit(seed, offset, bh_base + bh, i, j, T) ? inv_keep : 0.0;
                         dpr[j] = dot(doh + i * D, vh + j * D, D) * z;
                         PZ[i * N + j] = pr[j] * z;
                         dsum += pr[j] * dpr[j];
@@ -644,4 +647,21 @@ int oracle_attn_bwd_dropout(const double* q, const double* k, const double* v,
     free(PZ);
     free(dS);
     return fail;
+}
+
+/* The dropout entry points over a whole batch: decisions of slice bh drawn as
+ * head bh. */
+int oracle_attn_fwd_dropout(const double* q, const double* k, const double* v, double* o,
+                            double* lse, int64_t B, int64_t H, int64_t N, int64_t D,
+                            double scale, int causal, double p, uint64_t seed,
+                            uint64_t offset) {
+    return oracle_attn_fwd_dropout_bh(q, k, v, o, lse, B, H, N, D, scale, causal, p, seed,
+                                      offset, 0);
+}
+int oracle_attn_bwd_dropout(const double* q, const double* k, const double* v,
+                            const double* dout, double* dq, double* dk, double* dv,
+                            int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                            int causal, double p, uint64_t seed, uint64_t offset) {
+    return oracle_attn_bwd_dropout_bh(q, k, v, dout, dq, dk, dv, B, H, N, D, scale, causal,
+                                      p, seed, offset, 0);
 }

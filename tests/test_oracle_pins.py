@@ -599,3 +599,56 @@ def test_dropout_is_unbiased():
                      for seed in range(3000)])
     mean, se = runs.mean(axis=0), runs.std(axis=0) / math.sqrt(len(runs))
     assert (np.abs(mean - ref) < 5 * se + 1e-12).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_dropout_matches_torch_on_assembled_masks(causal):
+    """Packed dropout forward and backward against torch fp64 (forward and
+    autograd) over the whole packed axis: the allowed set is block diagonal
+    (causal inside each sequence) and sequence b of head h keeps the weights
+    dropout_mask(b * H + h, ...) keeps, positions counted from its start."""
+    lengths = [0, 29, 1, 40, 0, 17]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    H, total, D = 2, int(cu[-1]), 8
+    p, seed, offset = 0.25, 1234, 7
+    g = torch.Generator().manual_seed(37)
+    q, k, v, do = (torch.randn(H, total, D, generator=g, dtype=torch.float64)
+                   for _ in range(4))
+    scale = 0.35
+    allowed = torch.zeros(total, total, dtype=torch.bool)
+    z = torch.zeros(H, total, total, dtype=torch.float64)
+    inv_keep = 256.0 / (256.0 - oracle.dropout_threshold(p))
+    for b, n in enumerate(lengths):
+        s, e = int(cu[b]), int(cu[b + 1])
+        if n == 0:
+            continue
+        blk = torch.ones(n, n, dtype=torch.bool)
+        allowed[s:e, s:e] = blk.tril() if causal else blk
+        for h in range(H):
+            keep = oracle.dropout_mask(b * H + h, n, n, p, seed, offset)
+            z[h, s:e, s:e] = torch.from_numpy(keep.astype(np.float64)) * inv_keep
+    qa, ka, va = (x.clone().requires_grad_(True) for x in (q, k, v))
+    sc = (scale * torch.matmul(qa, ka.transpose(-1, -2))).masked_fill(~allowed, float("-inf"))
+    lse_ref = torch.logsumexp(sc, dim=-1)
+    o_ref = torch.matmul(torch.softmax(sc, dim=-1) * z, va)
+    o_ref.backward(do)
+    o, lse = oracle.fwd_varlen_dropout(q, k, v, cu, scale, causal, p, seed, offset)
+    assert np.abs(o - o_ref.detach().numpy()).max() < 1e-12
+    assert np.abs(lse - lse_ref.detach().numpy()).max() < 1e-12
+    grads = oracle.bwd_varlen_dropout(q, k, v, do, cu, scale, causal, p, seed, offset)
+    for ref, got in ((qa.grad, grads[0]), (ka.grad, grads[1]), (va.grad, grads[2])):
+        ref = ref.numpy()
+        assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 1e-12
+
+
+def test_packed_dropout_at_zero_is_the_packed_oracle():
+    cu = np.array([0, 33, 33, 90], dtype=np.int32)
+    g = torch.Generator().manual_seed(38)
+    q, k, v, do = (torch.randn(2, 90, 8, generator=g, dtype=torch.float64) for _ in range(4))
+    o0, l0 = oracle.fwd_varlen(q, k, v, cu, 0.3, True)
+    o1, l1 = oracle.fwd_varlen_dropout(q, k, v, cu, 0.3, True, 0.0, 5, 0)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    g0 = oracle.bwd_varlen(q, k, v, do, cu, 0.3, True)
+    g1 = oracle.bwd_varlen_dropout(q, k, v, do, cu, 0.3, True, 0.0, 5, 0)
+    for a, b in zip(g0, g1):
+        assert np.abs(a - b).max() < 1e-13
