@@ -79,8 +79,15 @@ def load() -> ctypes.CDLL:
                                    ctypes.c_size_t, _i, _i, _i, _i, _f, _i, _f, _u64, _u64,
                                    _vp]
     lib.fa_bwd_dropout.restype = _i
+    lib.fa_fwd_varlen_dropout.argtypes = lib.fa_fwd_varlen.argtypes[:-1] + [_f, _u64, _u64,
+                                                                            _vp]
+    lib.fa_fwd_varlen_dropout.restype = _i
+    lib.fa_bwd_varlen_dropout.argtypes = lib.fa_bwd_varlen.argtypes[:-1] + [_f, _u64, _u64,
+                                                                            _vp]
+    lib.fa_bwd_varlen_dropout.restype = _i
     for name in ("fa_fwd", "fa_fwd_qk", "fa_fwd_splitkv", "fa_fwd_varlen", "fa_bwd",
-                 "fa_bwd_varlen", "fa_fwd_dropout", "fa_bwd_dropout"):
+                 "fa_bwd_varlen", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_varlen_dropout",
+                 "fa_bwd_varlen_dropout"):
         f16 = getattr(lib, name + "_f16")  # the fp16 twin: same arguments
         f16.argtypes = getattr(lib, name).argtypes
         f16.restype = _i
@@ -273,9 +280,12 @@ def fa_fwd_splitkv(q, k, v, softmax_scale=None, causal=False, num_splits=0, out=
 
 
 def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None,
-                  causal=False, out=None, lse=None, return_lse=True, stream=None):
+                  causal=False, out=None, lse=None, return_lse=True, stream=None,
+                  dropout_p=0.0, seed=0, offset=0):
     """Packed forward.  q, k, v: bf16 [H, total, D]; cu_seqlens: int32 GPU
-    tensor [nseq + 1]; max_seqlen: host int >= the longest sequence.
+    tensor [nseq + 1]; max_seqlen: host int >= the longest sequence.  With
+    ``dropout_p`` > 0 the weights are dropped by fa_fwd_varlen_dropout's rule
+    (pass the same ``seed`` and ``offset`` to fa_bwd_varlen).
 
     Returns (o [H, total, D] bf16, lse [H, total] fp32 or None).
     """
@@ -295,10 +305,13 @@ def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None,
     if lse is None and return_lse:
         lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
     _check_lse(lse, (H, total), q.device)
-    rc = _fn("fa_fwd_varlen", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                              _ptr(cu_seqlens), nseq, total, int(max_seqlen), H, D,
-                              _scale(softmax_scale, D), int(bool(causal)),
-                              _stream(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens), nseq, total,
+            int(max_seqlen), H, D, _scale(softmax_scale, D), int(bool(causal)))
+    if dropout_p:
+        rc = _fn("fa_fwd_varlen_dropout", q)(*args, float(dropout_p), int(seed), int(offset),
+                                             _stream(stream))
+    else:
+        rc = _fn("fa_fwd_varlen", q)(*args, _stream(stream))
     if rc != 0:
         raise FaError(rc, "fa_fwd_varlen")
     return o, lse
@@ -351,7 +364,8 @@ def fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None,
 
 
 def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, softmax_scale=None,
-                  causal=False, dq=None, dk=None, dv=None, workspace=None, stream=None):
+                  causal=False, dq=None, dk=None, dv=None, workspace=None, stream=None,
+                  dropout_p=0.0, seed=0, offset=0):
     """Backward pass of fa_fwd_varlen.  q, k, v, o, dout: bf16 or fp16
     [H, total, D]; lse: fp32 [H, total] from fa_fwd_varlen on the same
     inputs; cu_seqlens: int32 GPU tensor [nseq + 1]; max_seqlen: host int >=
@@ -359,7 +373,8 @@ def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, softmax_scale=N
 
     Returns (dq, dk, dv) [H, total, D] in q's element type.  ``workspace``
     (GPU tensor of at least fa_bwd_workspace_size(1, H, total, D) bytes) is
-    allocated when not given.
+    allocated when not given.  ``dropout_p``, ``seed`` and ``offset`` must be
+    those of the forward pass, whose decisions are replayed.
     """
     torch = _torch()
     for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
@@ -384,11 +399,15 @@ def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, softmax_scale=N
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     _check_workspace(workspace, q.device)
-    rc = _fn("fa_bwd_varlen", q)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
-                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), nseq, total,
-                                 int(max_seqlen), _ptr(workspace),
-                                 workspace.numel() * workspace.element_size(), H, D,
-                                 _scale(softmax_scale, D), int(bool(causal)), _stream(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+            _ptr(dv), _ptr(cu_seqlens), nseq, total, int(max_seqlen), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), H, D, _scale(softmax_scale, D),
+            int(bool(causal)))
+    if dropout_p:
+        rc = _fn("fa_bwd_varlen_dropout", q)(*args, float(dropout_p), int(seed), int(offset),
+                                             _stream(stream))
+    else:
+        rc = _fn("fa_bwd_varlen", q)(*args, _stream(stream))
     if rc != 0:
         raise FaError(rc, "fa_bwd_varlen")
     return dq, dk, dv

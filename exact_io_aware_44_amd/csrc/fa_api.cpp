@@ -153,7 +153,7 @@ int fwd_splitkv_impl(bool f16, const void* q, const void* k, const void* v, void
 int fwd_varlen_impl(bool f16, const void* q, const void* k, const void* v, void* o,
                     float* lse, const int32_t* cu_seqlens, int nseq, int total,
                     int max_seqlen, int H, int D, float softmax_scale, int causal,
-                    hipStream_t stream) {
+                    hipStream_t stream, const fa::Dropout* drop = nullptr) {
     if (!q || !k || !v || !o || !cu_seqlens) return FA_ERR_NULL;
     if (nseq < 1 || total < 1 || max_seqlen < 1 || nseq > 65535) return FA_ERR_SHAPE;
     if (int rc = check_common(H, D, softmax_scale, causal)) return rc;
@@ -165,6 +165,7 @@ int fwd_varlen_impl(bool f16, const void* q, const void* k, const void* v, void*
     if (max_seqlen > total) max_seqlen = total;  // no sequence is longer than total
     fa::FwdArgs a{q, k, v, o, lse, cu_seqlens, nseq, H, total, max_seqlen, D,
                   softmax_scale, causal != 0, total};
+    if (drop) a.drop = *drop;
     a.f16 = f16;
     return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -196,7 +197,7 @@ int bwd_varlen_impl(bool f16, const void* q, const void* k, const void* v, const
                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
                     const int32_t* cu_seqlens, int nseq, int total, int max_seqlen,
                     void* workspace, size_t ws_bytes, int H, int D, float softmax_scale,
-                    int causal, hipStream_t stream) {
+                    int causal, hipStream_t stream, const fa::Dropout* drop = nullptr) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !cu_seqlens)
         return FA_ERR_NULL;
     if (nseq < 1 || total < 1 || max_seqlen < 1 || nseq > 65535) return FA_ERR_SHAPE;
@@ -216,6 +217,7 @@ int bwd_varlen_impl(bool f16, const void* q, const void* k, const void* v, const
     a.f16 = f16;
     a.cu = cu_seqlens;
     a.max_seqlen = max_seqlen;
+    if (drop) a.drop = *drop;
     return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -358,6 +360,28 @@ int fa_bwd_varlen_f16(const void* q, const void* k, const void* v, const void* o
         if (int rc = make_dropout(dropout_p, seed, offset, d)) return rc;                  \
         return bwd_impl(F16, q, k, v, o, lse, dout, dq, dk, dv, workspace, ws_bytes, B, H,  \
                         N, D, softmax_scale, causal, stream, &d);                          \
+    }                                                                                      \
+    int fa_fwd_varlen_dropout##SUFFIX(                                                     \
+        const void* q, const void* k, const void* v, void* o, float* lse,                  \
+        const int32_t* cu_seqlens, int nseq, int total, int max_seqlen, int H, int D,      \
+        float softmax_scale, int causal, float dropout_p, uint64_t seed, uint64_t offset,  \
+        hipStream_t stream) {                                                              \
+        fa::Dropout d{};                                                                   \
+        if (int rc = make_dropout(dropout_p, seed, offset, d)) return rc;                  \
+        return fwd_varlen_impl(F16, q, k, v, o, lse, cu_seqlens, nseq, total, max_seqlen,  \
+                               H, D, softmax_scale, causal, stream, &d);                   \
+    }                                                                                      \
+    int fa_bwd_varlen_dropout##SUFFIX(                                                     \
+        const void* q, const void* k, const void* v, const void* o, const float* lse,      \
+        const void* dout, void* dq, void* dk, void* dv, const int32_t* cu_seqlens,         \
+        int nseq, int total, int max_seqlen, void* workspace, size_t ws_bytes, int H,      \
+        int D, float softmax_scale, int causal, float dropout_p, uint64_t seed,            \
+        uint64_t offset, hipStream_t stream) {                                             \
+        fa::Dropout d{};                                                                   \
+        if (int rc = make_dropout(dropout_p, seed, offset, d)) return rc;                  \
+        return bwd_varlen_impl(F16, q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, nseq,   \
+                               total, max_seqlen, workspace, ws_bytes, H, D,               \
+                               softmax_scale, causal, stream, &d);                         \
     }
 FA_DROPOUT_ENTRIES(, false)
 FA_DROPOUT_ENTRIES(_f16, true)

@@ -779,14 +779,12 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream) {
 
 template <typename E, bool DROP>
 hipError_t run_bwd_d(const BwdArgs& a, hipStream_t stream) {
-    if constexpr (!DROP) {
-        if (a.cu) {  // packed sequences (no dropout on this path)
-            if (a.D == 64)
-                return a.causal ? run_bwd<E, 64, true, false, true>(a, stream)
-                                : run_bwd<E, 64, false, false, true>(a, stream);
-            return a.causal ? run_bwd<E, 128, true, false, true>(a, stream)
-                            : run_bwd<E, 128, false, false, true>(a, stream);
-        }
+    if (a.cu) {  // packed sequences
+        if (a.D == 64)
+            return a.causal ? run_bwd<E, 64, true, DROP, true>(a, stream)
+                            : run_bwd<E, 64, false, DROP, true>(a, stream);
+        return a.causal ? run_bwd<E, 128, true, DROP, true>(a, stream)
+                        : run_bwd<E, 128, false, DROP, true>(a, stream);
     }
     if (a.D == 64)
         return a.causal ? run_bwd<E, 64, true, DROP>(a, stream)

@@ -935,9 +935,13 @@ hipError_t run_fwd_d(const FwdArgs& a, hipStream_t stream) {
     if (a.decode)
         return a.causal ? run_decode<E, D, true>(a, stream) : run_decode<E, D, false>(a, stream);
     const bool varlen = a.cu != nullptr;
-    if (a.drop.thresh > 0)  // dropout: dense batch only
+    if (a.drop.thresh > 0) {  // dropout: dense batch or packed sequences
+        if (varlen)
+            return a.causal ? run_fwd<E, D, true, true, false, true>(a, stream)
+                            : run_fwd<E, D, false, true, false, true>(a, stream);
         return a.causal ? run_fwd<E, D, true, false, false, true>(a, stream)
                         : run_fwd<E, D, false, false, false, true>(a, stream);
+    }
     if (a.splits > 1)
         return a.causal ? run_fwd<E, D, true, false, true>(a, stream)
                         : run_fwd<E, D, false, false, true>(a, stream);

@@ -258,8 +258,13 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
  *   offset      generator counter offset (low 32 bits used); advance it per
  *               call to draw fresh masks under one seed
  *
- * Other arguments, layouts and status codes are those of fa_fwd and fa_bwd
- * (dense batch only).
+ * Other arguments, layouts and status codes are those of fa_fwd and fa_bwd.
+ *
+ * The packed variants (fa_fwd_varlen_dropout, fa_bwd_varlen_dropout) apply
+ * the same rule to each sequence b of head h of a packed batch, with
+ * counter (key / 4, query / 4, b * H + h, offset mod 2^32), query and key
+ * counted from the sequence start; their other arguments are those of
+ * fa_fwd_varlen and fa_bwd_varlen.
  */
 int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                    int H, int N, int D, float softmax_scale, int causal, float dropout_p,
@@ -269,6 +274,16 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
                    void* workspace, size_t workspace_bytes, int B, int H, int N, int D,
                    float softmax_scale, int causal, float dropout_p, uint64_t seed,
                    uint64_t offset, hipStream_t stream);
+int fa_fwd_varlen_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int32_t* cu_seqlens, int nseq, int total, int max_seqlen,
+                          int H, int D, float softmax_scale, int causal, float dropout_p,
+                          uint64_t seed, uint64_t offset, hipStream_t stream);
+int fa_bwd_varlen_dropout(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          const int32_t* cu_seqlens, int nseq, int total, int max_seqlen,
+                          void* workspace, size_t workspace_bytes, int H, int D,
+                          float softmax_scale, int causal, float dropout_p, uint64_t seed,
+                          uint64_t offset, hipStream_t stream);
 
 /*
  * FP16 variants (nexusofnerds "What is FlashAttention?": the kernels run in
@@ -308,6 +323,17 @@ int fa_bwd_dropout_f16(const void* q, const void* k, const void* v, const void* 
                        void* workspace, size_t workspace_bytes, int B, int H, int N, int D,
                        float softmax_scale, int causal, float dropout_p, uint64_t seed,
                        uint64_t offset, hipStream_t stream);
+int fa_fwd_varlen_dropout_f16(const void* q, const void* k, const void* v, void* o,
+                              float* lse, const int32_t* cu_seqlens, int nseq, int total,
+                              int max_seqlen, int H, int D, float softmax_scale, int causal,
+                              float dropout_p, uint64_t seed, uint64_t offset,
+                              hipStream_t stream);
+int fa_bwd_varlen_dropout_f16(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk,
+                              void* dv, const int32_t* cu_seqlens, int nseq, int total,
+                              int max_seqlen, void* workspace, size_t workspace_bytes, int H,
+                              int D, float softmax_scale, int causal, float dropout_p,
+                              uint64_t seed, uint64_t offset, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -36,12 +36,14 @@ def _declared():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert names == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_dropout_f16", "fa_bwd_f16",
-                     "fa_bwd_varlen", "fa_bwd_varlen_f16",
+                     "fa_bwd_varlen", "fa_bwd_varlen_dropout", "fa_bwd_varlen_dropout_f16",
+                     "fa_bwd_varlen_f16",
                      "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_dropout",
                      "fa_fwd_dropout_f16", "fa_fwd_f16", "fa_fwd_qk", "fa_fwd_qk_f16",
                      "fa_fwd_splitkv",
                      "fa_fwd_splitkv_f16", "fa_fwd_splitkv_workspace_size",
-                     "fa_fwd_varlen", "fa_fwd_varlen_f16", "fa_status_string"]
+                     "fa_fwd_varlen", "fa_fwd_varlen_dropout", "fa_fwd_varlen_dropout_f16",
+                     "fa_fwd_varlen_f16", "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -210,6 +212,22 @@ def bwd_varlen(lib, q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, cu=P, nse
 ])
 def test_bwd_varlen_rejects(lib, kw, code):
     assert bwd_varlen(lib, **kw) == code
+
+
+@pytest.mark.parametrize("p,code", [(-0.1, ARG), (1.0, ARG), (float("nan"), ARG)])
+def test_varlen_dropout_rejects_probability(lib, p, code):
+    assert lib.fa_fwd_varlen_dropout(P, P, P, P, P, P, 2, 32, 16, 2, 128, 0.1, 1, p, 1, 0,
+                                     None) == code
+    assert lib.fa_bwd_varlen_dropout(P, P, P, P, P, P, P, P, P, P, 2, 32, 16, P, 1 << 20, 2,
+                                     128, 0.1, 1, p, 1, 0, None) == code
+
+
+def test_varlen_dropout_validates_like_varlen(lib):
+    # one invalid argument each: the packed checks run after the dropout ones
+    assert lib.fa_fwd_varlen_dropout(P, P, P, P, P, None, 2, 32, 16, 2, 128, 0.1, 1, 0.1, 1, 0,
+                                     None) == NULL
+    assert lib.fa_bwd_varlen_dropout(P, P, P, P, P, P, P, P, P, P, 2, 32, 16, P, 100, 2, 128,
+                                     0.1, 1, 0.1, 1, 0, None) == WS
 
 
 def test_bwd_varlen_workspace_is_dense_size_of_packed_rows(lib):
