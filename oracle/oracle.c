@@ -75,9 +75,9 @@
  *   - key j is kept for query i iff u >= T, T = min(255, round(256 p)), so
  *     the dropout probability is p' = T / 256 and kept weights are scaled by
  *     256 / (256 - T).
- * The generator's output stream is parity unpinned against other
- * implementations (no reference vectors are used); the tests pin its
- * statistics and every use of it.
+ * The generator's output stream is pinned by the known-answer vectors
+ * published with Philox4x32-10 (tests/golden/philox4x32_10_kat.txt); the
+ * tests also check its statistics and pin every use of it.
  *
  * Build: gcc -O2 -fopenmp -fPIC -shared oracle.c -lm   (no -ffast-math).
  */

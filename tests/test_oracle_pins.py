@@ -515,10 +515,30 @@ def test_key_split_partials_merge_by_lse():
 
 # --------------------------------------------------------------------------
 # Attention dropout (tensortonic section 7: the backward replays the forward's
-# drop decisions).  The generator is this library's definition (Philox4x32-10
-# as published by Salmon et al.); its stream is pinned by its statistics, and
-# every use of it by closed forms and library routines on the same mask.
+# drop decisions).  The generator is Philox4x32-10 as published by Salmon et
+# al.; its stream is pinned by the published known-answer vectors, its
+# statistics are checked besides, and every use of it is pinned by closed
+# forms and library routines on the same mask.
 # --------------------------------------------------------------------------
+def test_philox_known_answer_vectors():
+    """The oracle's generator reproduces the known-answer vectors published
+    with Philox4x32-10 (tests/golden/philox4x32_10_kat.txt): a wrong round
+    multiplier, key increment, round count or output word order fails them."""
+    n = 0
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            lhs, rhs = line.split("->")
+            words = [int(x, 16) for x in lhs.split()]
+            want = [int(x, 16) for x in rhs.split()]
+            got = [int(x) for x in oracle.philox4x32_10(words[:4], words[4:])]
+            assert got == want, (line, ["%08x" % x for x in got])
+            n += 1
+    assert n == 3
+
+
 def test_philox_statistics_and_injectivity():
     outs = np.array([oracle.philox4x32_10([c, 7, 3, 0], [11, 22]) for c in range(4096)],
                     dtype=np.uint64)
