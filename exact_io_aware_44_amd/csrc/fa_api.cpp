@@ -64,23 +64,27 @@ struct Splits {
     int count;
     int chunk;  // keys per range
 };
+// All arithmetic is in int64: the sizes come straight from the caller.
 Splits pick_splits(int B, int H, int Nq, int Nk, int requested) {
-    const int64_t units = (int64_t)B * H * ((Nq + 127) / 128);
+    const int64_t nq = Nq, nk = Nk;
+    const int64_t units = (int64_t)B * H * ((nq + 127) / 128);
     int64_t s = requested;
-    if (s == 0 && Nq <= kDecodeMaxQ) {
+    if (s == 0 && nq <= kDecodeMaxQ) {
         // decoding kernel: one workgroup per CU (256 of them), each range at
         // least 512 keys so every wave streams several blocks
         s = std::min<int64_t>(128, (256 + units - 1) / units);
-        s = std::min<int64_t>(s, std::max(1, (Nk + 511) / 512));
+        s = std::min<int64_t>(s, std::max<int64_t>(1, (nk + 511) / 512));
     } else if (s == 0) {
         s = std::min<int64_t>(128, (512 + units - 1) / units);
-        s = std::min<int64_t>(s, std::max(1, (Nk + 255) / 256));
+        s = std::min<int64_t>(s, std::max<int64_t>(1, (nk + 255) / 256));
     }
-    s = std::max<int64_t>(1, std::min<int64_t>(s, (Nk + 63) / 64));
-    const int chunk = (int)(((Nk + s - 1) / s + 63) / 64 * 64);
-    return Splits{(Nk + chunk - 1) / chunk, chunk};
+    s = std::max<int64_t>(1, std::min<int64_t>(s, (nk + 63) / 64));
+    const int64_t chunk = ((nk + s - 1) / s + 63) / 64 * 64;
+    return Splits{(int)((nk + chunk - 1) / chunk), (int)chunk};
 }
-// Partial O then partial L, fp32, each region padded to 256 bytes.
+// Partial O then partial L, fp32, each region padded to 256 bytes.  The
+// sizes are already validated (B, H <= 65535, one slice below 2 GiB, at most
+// one range per 64 keys), so the products stay far below 2^64.
 size_t splitkv_bytes(int B, int H, int Nq, int D, int splits) {
     if (splits <= 1) return 0;
     const size_t rows = (size_t)B * H * Nq * splits;
@@ -248,13 +252,18 @@ const char* fa_status_string(int status) {
 }
 
 size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int D, int num_splits) {
-    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || num_splits < 0 || (D != 64 && D != 128))
+    // sizes fa_fwd_splitkv would reject need no workspace
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || num_splits < 0 || (D != 64 && D != 128) ||
+        B > 65535 || H > 65535 || check_slice(Nk, D) || check_slice(2 * (int64_t)Nq, D))
         return 0;
     return splitkv_bytes(B, H, Nq, D, pick_splits(B, H, Nq, Nk, num_splits).count);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int D) {
-    if (B < 1 || H < 1 || N < 1 || (D != 64 && D != 128)) return 0;
+    // sizes fa_bwd would reject need no workspace
+    if (B < 1 || H < 1 || N < 1 || (D != 64 && D != 128) || B > 65535 || H > 65535 ||
+        check_slice(N, D))
+        return 0;
     return workspace_bytes(B, H, N);
 }
 

@@ -24,6 +24,13 @@
  *  - softmax_scale multiplies the float32 dot product q_i . k_j before the
  *    softmax (tensortonic section 6 divides by sqrt(head width); pass
  *    1/sqrt(D) for that).  It must be finite and > 0.
+ *  - Inputs must be finite: every element of q, k, v (and of o, lse and dout
+ *    passed to a backward entry) must be a finite number, and the scaled
+ *    scores must stay within float32 range.  The forward kernels are compiled
+ *    on that assumption (their maxima skip NaN handling), so a NaN or
+ *    infinite input yields unspecified output: it is not guaranteed to
+ *    propagate as NaN.  Masked positions use -infinity internally, never
+ *    NaN, and rows that read no key produce O = 0 and L = -infinity.
  *  - L is in natural-log units of the scaled scores: L_i = ln sum_j
  *    exp(scale * q_i . k_j) over the allowed keys (tensortonic section 7).
  *  - Supported head widths: D = 64 and D = 128.
@@ -113,7 +120,10 @@ int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of device workspace fa_fwd_splitkv needs for these sizes and this
- * num_splits (0 when it will not split, or when the sizes are invalid).
+ * num_splits (0 when it will not split, or when fa_fwd_splitkv would reject
+ * the sizes).  It holds each key range's normalised partial O_s and L_s
+ * (float32) until the merge, L = ln sum_s exp(L_s) (tensortonic section 5's
+ * running rescale applied to whole key ranges).
  */
 size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int D, int num_splits);
 
@@ -176,10 +186,13 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
                   int causal, hipStream_t stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes (0 if the sizes
- * are invalid).  The workspace holds two float32 values per query row,
- * D_i = <dO_i, O_i> and -L_i * log2(e), as two [B, H, N] regions each
- * padded to 256 bytes.
+ * Bytes of device workspace fa_bwd needs for these sizes (0 if fa_bwd would
+ * reject the sizes).  tensortonic section 7: the backward pass rebuilds each
+ * weight as exp(s_ij - L_i) from the row statistic L saved by the forward
+ * pass; the workspace holds that statistic per query row in the form the
+ * kernels use, -L_i * log2(e), and the row sum D_i = <dO_i, O_i> of the
+ * softmax gradient, as two float32 [B, H, N] regions each padded to 256
+ * bytes.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int D);
 
@@ -335,7 +348,11 @@ int fa_bwd_varlen_dropout_f16(const void* q, const void* k, const void* v, const
                               int D, float softmax_scale, int causal, float dropout_p,
                               uint64_t seed, uint64_t offset, hipStream_t stream);
 
-/* Static, human-readable name of a status code (never NULL). */
+/*
+ * Static, human-readable name of a status code (never NULL; "unknown fa
+ * status" for a value outside enum fa_status).  A library convention for
+ * error reporting, not part of the method the pages describe.
+ */
 const char* fa_status_string(int status);
 
 #ifdef __cplusplus

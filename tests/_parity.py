@@ -56,6 +56,44 @@ def rel_l2(got, ref) -> float:
     return float(num / den) if den > 0 else float(num)
 
 
+# Rows per block of the blockwise gradient check: the kernels' query stage
+# and key-tile granularity, so one bad stage or ragged row cannot hide in the
+# norm of a whole (batch, head) slice.
+GRAD_BLOCK_ROWS = 64
+
+
+def check_grad(got, ref, what="", cu=None, block_rows=GRAD_BLOCK_ROWS):
+    """Relative L2 error of a gradient tensor, over the whole tensor and over
+    every block of ``block_rows`` consecutive rows of each leading index
+    (rows are the second-to-last axis).  With packed offsets ``cu`` the blocks
+    start at each sequence's first row and stop at its end.  Each must be
+    <= GRAD_REL_L2; returns (whole, worst block)."""
+    got = f64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), what + ": non-finite gradient"
+    whole = rel_l2(got, ref)
+    n, d = ref.shape[-2], ref.shape[-1]
+    g2 = got.reshape(-1, n, d)
+    r2 = ref.reshape(-1, n, d)
+    if cu is None:
+        segs = [(0, n)]
+    else:
+        c = [int(x) for x in cu]
+        segs = [(a, b) for a, b in zip(c[:-1], c[1:]) if b > a]
+    worst, at = 0.0, None
+    for s in range(r2.shape[0]):
+        for a, b in segs:
+            for r0 in range(a, b, block_rows):
+                r1 = min(b, r0 + block_rows)
+                e = rel_l2(g2[s, r0:r1], r2[s, r0:r1])
+                if e > worst:
+                    worst, at = e, (s, r0)
+    assert whole <= GRAD_REL_L2, (what, "whole", whole)
+    assert worst <= GRAD_REL_L2, (what, "block (slice, row0)", at, worst)
+    return whole, worst
+
+
 def oracle_rows_dense(q, k, v, scale, causal, bh, rows):
     """Oracle O and L for flattened heads bh[t] = b*H + h and rows rows[t].
 

@@ -1,13 +1,12 @@
 """GPU parity of the backward pass (fa_bwd) against the fp64 oracle gradients.
 
 O and L come from the library's own forward pass, as the ABI requires."""
-import numpy as np
 import pytest
 import torch
 
 import attn_inputs as ai
 import oracle
-from _parity import GRAD_REL_L2, rel_l2, say
+from _parity import check_grad, say
 
 pytestmark = pytest.mark.gpu
 
@@ -22,12 +21,11 @@ def _fwd_bwd(fa, q, k, v, do, scale, causal):
 
 
 def _check(got, ref, what):
-    errs = [rel_l2(g, r) for g, r in zip(got, ref)]
-    say("  %s: rel-L2 dQ %.3e dK %.3e dV %.3e" % (what, *errs))
-    for name, e in zip(("dQ", "dK", "dV"), errs):
-        assert e <= GRAD_REL_L2, (what, name, e)
-    for g in got:
-        assert torch.isfinite(g).all(), what
+    """Whole-tensor and per-64-row-block relative L2 of dQ, dK and dV."""
+    errs = [check_grad(g, r, "%s %s" % (what, name))
+            for name, g, r in zip(("dQ", "dK", "dV"), got, ref)]
+    say("  %s: rel-L2 (whole / worst 64-row block) dQ %.3e / %.3e  dK %.3e / %.3e"
+        "  dV %.3e / %.3e" % (what, *[x for e in errs for x in e]))
 
 
 # N = 300 and 960 at D = 128 leave an odd number of interior 64-query stages
@@ -58,20 +56,18 @@ def test_deterministic(gpu):
         assert torch.equal(x, y)
 
 
-def test_backward_workload_sampled_heads(gpu):
-    """B2 H32 N4096 D128 causal (full launch); the oracle's exact gradients
-    for three seeded (batch, head) slices are compared element by element."""
+def test_backward_workload_full_oracle(gpu):
+    """B2 H32 N4096 D128 causal (the benchmark's launch): every one of the 64
+    (batch, head) slices against the oracle's exact gradients, element by
+    element, per slice and per 64-row block."""
     w = ai.BACKWARD
     say("case", w.name)
     q, k, v, do = ai.backward_inputs()
     got = _fwd_bwd(gpu, q, k, v, do, w.scale, True)
-    g = ai.generator(50)
-    picks = [(int(torch.randint(0, w.B, (1,), generator=g)),
-              int(torch.randint(0, w.H, (1,), generator=g))) for _ in range(3)]
-    for b, h in picks:
-        sl = (slice(b, b + 1), slice(h, h + 1))
+    for b in range(w.B):
+        sl = slice(b, b + 1)
         ref = oracle.bwd(q[sl], k[sl], v[sl], do[sl], w.scale, True)
-        _check([x[sl] for x in got], ref, "%s b%d h%d" % (w.name, b, h))
+        _check([x[sl] for x in got], ref, "%s b%d (all %d heads)" % (w.name, b, w.H))
 
 
 @pytest.mark.parametrize("causal", [False, True])

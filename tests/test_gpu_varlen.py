@@ -1,11 +1,10 @@
 """GPU parity of the packed variable-length forward pass (fa_fwd_varlen)."""
-import numpy as np
 import pytest
 import torch
 
 import attn_inputs as ai
 import oracle
-from _parity import check_fwd, f64, oracle_rows_varlen, say
+from _parity import check_fwd, say
 
 pytestmark = pytest.mark.gpu
 
@@ -64,19 +63,17 @@ def test_packed_equals_separate_runs_bitwise(gpu):
             assert torch.equal(lse[:, sl], ld[0].cpu()), (b, n, causal)
 
 
-def test_varlen_workload_full_size_sampled(gpu):
+def test_varlen_workload_full_oracle(gpu):
     """16 sequences with lengths ~ U[128, 8192] (seeded), H32 D128, causal:
-    256 seeded (head, token) pairs plus the first and last token of every
-    sequence (in every other head), against full oracle rows."""
+    every element of O and every row of L against the oracle, eight heads at
+    a time (about 2.9e12 fp64 flops in all)."""
     q, k, v, cu, lengths = ai.varlen_inputs()
     H, total, D = q.shape
     say("case", ai.VARLEN_NAME, "total", total)
     scale = ai.default_scale(D)
     o, lse = _run(gpu, q, k, v, cu, max(lengths), scale, True)
-    extra = []
-    for b in range(len(lengths)):
-        extra += [(b % H, int(cu[b])), ((b + 5) % H, int(cu[b + 1]) - 1)]
-    heads, toks = ai.sample_rows(11, H, total, 256, extra=extra)
-    o_ref, l_ref = oracle_rows_varlen(q, k, v, cu, scale, True, heads, toks)
-    check_fwd(o[heads, toks], lse[heads, toks], o_ref, l_ref, ai.VARLEN_NAME)
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    for h0 in range(0, H, 8):
+        sl = slice(h0, h0 + 8)
+        o_ref, l_ref = oracle.fwd_varlen(q[sl], k[sl], v[sl], cu, scale, True)
+        check_fwd(o[sl], lse[sl], o_ref, l_ref, "%s heads %d-%d" % (ai.VARLEN_NAME, h0, h0 + 7))

@@ -1,11 +1,10 @@
 """GPU parity of the packed variable-length backward pass (fa_bwd_varlen)."""
-import numpy as np
 import pytest
 import torch
 
 import attn_inputs as ai
 import oracle
-from _parity import GRAD_REL_L2, rel_l2, say
+from _parity import check_grad, say
 
 pytestmark = pytest.mark.gpu
 
@@ -42,10 +41,8 @@ def test_small_full_oracle(gpu, lengths, causal, D):
     got = _grads(gpu, q, k, v, do, cu, max(lengths), scale, causal)
     refs = oracle.bwd_varlen(q, k, v, do, cu, scale, causal)
     for name, g_, r in zip(("dQ", "dK", "dV"), got, refs):
-        assert torch.isfinite(g_.float()).all(), (lengths, name)
-        e = rel_l2(g_, r)
-        say("  %s rel-L2 %.3e" % (name, e))
-        assert e <= GRAD_REL_L2, (lengths, causal, D, name, e)
+        say("  %s rel-L2 whole %.3e, worst 64-row block %.3e"
+            % (name, *check_grad(g_, r, "%s %s %s" % (lengths, causal, name), cu=cu)))
 
 
 def test_packed_equals_separate_runs_bitwise(gpu):
@@ -84,9 +81,8 @@ def test_fp16(gpu):
     assert all(x.dtype == torch.float16 for x in got)
     refs = oracle.bwd_varlen(q, k, v, do, cu, scale, True)
     for name, g_, r in zip(("dQ", "dK", "dV"), got, refs):
-        e = rel_l2(g_, r)
-        say("  fp16 %s rel-L2 %.3e" % (name, e))
-        assert e <= GRAD_REL_L2, (name, e)
+        say("  fp16 %s rel-L2 whole %.3e, worst 64-row block %.3e"
+            % (name, *check_grad(g_, r, "fp16 " + name, cu=cu)))
 
 
 def test_varlen_workload_full_size_sampled_heads(gpu):
@@ -105,6 +101,5 @@ def test_varlen_workload_full_size_sampled_heads(gpu):
         sl = slice(h, h + 1)
         refs = oracle.bwd_varlen(q[sl], k[sl], v[sl], do[sl], cu, scale, True)
         for name, g_, r in zip(("dQ", "dK", "dV"), got, refs):
-            e = rel_l2(g_[sl], r)
-            say("  head %d %s rel-L2 %.3e" % (h, name, e))
-            assert e <= GRAD_REL_L2, (h, name, e)
+            say("  head %d %s rel-L2 whole %.3e, worst 64-row block %.3e"
+                % (h, name, *check_grad(g_[sl], r, "head %d %s" % (h, name), cu=cu)))

@@ -7,7 +7,7 @@ import torch
 
 import attn_inputs as ai
 import oracle
-from _parity import GRAD_REL_L2, check_fwd, f64, rel_l2, say
+from _parity import check_fwd, check_grad, f64, say
 from test_gpu_dropout import _code_basis, _codes_from_mask
 
 pytestmark = pytest.mark.gpu
@@ -68,9 +68,8 @@ def test_packed_forward_backward_full_oracle(gpu, causal, D):
     check_fwd(o.cpu(), lse.cpu(), o_ref, l_ref, "packed dropout %s" % lengths)
     refs = oracle.bwd_varlen_dropout(q, k, v, do, cu, scale, causal, p, seed, offset)
     for name, got, want in zip(("dQ", "dK", "dV"), grads, refs):
-        e = rel_l2(got.cpu(), want)
-        say("  %s rel-L2 %.3e" % (name, e))
-        assert torch.isfinite(got).all() and e <= GRAD_REL_L2, (name, e)
+        say("  %s rel-L2 whole %.3e, worst 64-row block %.3e"
+            % (name, *check_grad(got.cpu(), want, "packed dropout " + name, cu=cu)))
 
 
 def test_packed_fp16_dropout(gpu):
@@ -92,4 +91,4 @@ def test_packed_fp16_dropout(gpu):
     check_fwd(o.cpu(), lse.cpu(), o_ref, l_ref, "packed fp16 dropout")
     refs = oracle.bwd_varlen_dropout(q, k, v, do, cu, scale, True, p, seed, offset)
     for name, got, want in zip(("dQ", "dK", "dV"), grads, refs):
-        assert rel_l2(got.cpu(), want) <= GRAD_REL_L2, name
+        check_grad(got.cpu(), want, "packed fp16 dropout " + name, cu=cu)
