@@ -16,7 +16,7 @@ import os
 
 __all__ = ["load", "build", "FaError", "fa_fwd", "fa_fwd_qk", "fa_fwd_splitkv",
            "fa_fwd_splitkv_workspace_size", "fa_fwd_varlen", "fa_bwd", "fa_bwd_varlen",
-           "fa_bwd_workspace_size", "fa_status_string", "LIB_PATH"]
+           "fa_bwd_workspace_size", "fa_bwd_noalloc", "fa_status_string", "LIB_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
@@ -69,6 +69,9 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
                                   _i, _vp, ctypes.c_size_t, _i, _i, _f, _i, _vp]
     lib.fa_bwd_varlen.restype = _i
+    lib.fa_bwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
+                                   _i, _f, _i, _vp]
+    lib.fa_bwd_noalloc.restype = _i
     lib.fa_status_string.argtypes = [_i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _u64 = ctypes.c_uint64
@@ -360,6 +363,38 @@ def fa_bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None,
                               _scale(softmax_scale, D), int(bool(causal)), _stream(stream))
     if rc != 0:
         raise FaError(rc, "fa_bwd")
+    return dq, dk, dv
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None,
+                   dk=None, dv=None, stream=None):
+    """fa_bwd without a workspace: the library's static device scratch holds
+    it (bf16 only; B * H * N <= 2**21 rows).  With dq, dk and dv given the
+    call allocates nothing; calls that overlap on one GPU race.
+
+    Returns (dq, dk, dv) [B, H, N, D] bf16.
+    """
+    torch = _torch()
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check(t, name, q.shape, q.dtype)
+    B, H, N, D = q.shape
+    if lse is None:
+        raise ValueError("lse from fa_fwd is required")
+    _check_lse(lse, (B, H, N), q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, name, q.shape, q.dtype)
+    _same_device(q, (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"),
+                 (dv, "dv"))
+    if q.dtype != torch.bfloat16:
+        raise ValueError("fa_bwd_noalloc takes bfloat16 tensors")
+    rc = load().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                               _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, D,
+                               _scale(softmax_scale, D), int(bool(causal)), _stream(stream))
+    if rc != 0:
+        raise FaError(rc, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

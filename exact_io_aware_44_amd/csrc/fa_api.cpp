@@ -197,6 +197,29 @@ int bwd_impl(bool f16, const void* q, const void* k, const void* v, const void* 
     return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// fa_bwd without a workspace argument: the workspace lives in the library's
+// static device scratch (fa::kBwdScratchBytes per device).
+int bwd_noalloc_impl(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                     int H, int N, int D, float softmax_scale, int causal,
+                     hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+    if (B < 1 || N < 1) return FA_ERR_SHAPE;
+    if (int rc = check_common(H, D, softmax_scale, causal)) return rc;
+    if (B > 65535 || H > 65535) return FA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+        !aligned16(dv))
+        return FA_ERR_ALIGN;
+    if (int rc = check_slice(N, D)) return rc;
+    if (workspace_bytes(B, H, N) > fa::kBwdScratchBytes) return FA_ERR_SCRATCH;
+    float* ws = nullptr;
+    if (fa::bwd_scratch(&ws) != hipSuccess) return FA_ERR_LAUNCH;
+    fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, N, D, softmax_scale,
+                  causal != 0};
+    return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 int bwd_varlen_impl(bool f16, const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
                     const int32_t* cu_seqlens, int nseq, int total, int max_seqlen,
@@ -247,6 +270,9 @@ const char* fa_status_string(int status) {
                    "dropout_p in [0, 1)";
         case FA_ERR_TOO_LARGE:
             return "FA_ERR_TOO_LARGE: one (batch, head) slice exceeds 2 GiB";
+        case FA_ERR_SCRATCH:
+            return "FA_ERR_SCRATCH: B * H * N exceeds the 2^21 query rows of "
+                   "fa_bwd_noalloc's static scratch";
         default: return "unknown fa status";
     }
 }
@@ -321,6 +347,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            hipStream_t stream) {
     return bwd_impl(false, q, k, v, o, lse, dout, dq, dk, dv, workspace, ws_bytes, B, H, N,
                     D, softmax_scale, causal, stream);
+}
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                   int H, int N, int D, float softmax_scale, int causal, hipStream_t stream) {
+    return bwd_noalloc_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, softmax_scale,
+                            causal, stream);
 }
 int fa_bwd_f16(const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dout, void* dq, void* dk, void* dv, void* workspace,

@@ -31,6 +31,7 @@
 // queries (dV^T = dO^T P, dK^T = Q^T dS); their A operands (dO^T, Q^T) are
 // transpose reads of the row-major LDS tiles.  The dq pass mirrors the
 // forward kernel (lane = query).
+#include <mutex>
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -801,6 +802,36 @@ hipError_t run_bwd_e(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     return a.f16 ? run_bwd_e<f16>(a, stream) : run_bwd_e<bf16>(a, stream);
+}
+
+// ---- static scratch for the backward entry point that allocates nothing ----
+//
+// The backward's only scratch memory is its workspace (D_i and -L_i log2 e
+// per query row).  fa_bwd_noalloc takes it from this array instead of a
+// caller buffer: every GPU the library runs on holds its own copy, at its own
+// address, until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it is only a stand-in symbol): it looks up the
+// device address once per device with hipGetSymbolAddress and uses that.
+static __device__ __align__(256) unsigned char scratch[kBwdScratchBytes];
+
+hipError_t bwd_scratch(float** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {  // first call on this device: it is the current one
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = static_cast<float*>(addr[dev]);
+    return hipSuccess;
 }
 
 }  // namespace fa

@@ -63,4 +63,11 @@ struct BwdArgs {
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
+// Size of the static device scratch behind fa_bwd_noalloc: the backward
+// workspace of up to 2^21 query rows (B * H * N), two padded fp32 regions.
+constexpr size_t kBwdScratchBytes = (size_t)16 << 20;
+// Device address of that scratch on the current device (looked up once per
+// device, then cached).
+hipError_t bwd_scratch(float** ptr);
+
 }  // namespace fa

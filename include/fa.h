@@ -71,7 +71,9 @@ enum fa_status {
     FA_ERR_LAUNCH = 6,      /* a kernel launch failed (HIP error)              */
     FA_ERR_ARG = 7,         /* softmax_scale not finite or not > 0, a negative
                                num_splits, or dropout_p outside [0, 1)        */
-    FA_ERR_TOO_LARGE = 8    /* a (batch, head) slice exceeds 2 GiB             */
+    FA_ERR_TOO_LARGE = 8,   /* a (batch, head) slice exceeds 2 GiB             */
+    FA_ERR_SCRATCH = 9      /* fa_bwd_noalloc: B * H * N above its static
+                               scratch (2^21 query rows)                      */
 };
 
 /*
@@ -215,6 +217,25 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dout, void* dq, void* dk, void* dv,
            void* workspace, size_t workspace_bytes, int B, int H, int N, int D,
            float softmax_scale, int causal, hipStream_t stream);
+
+/*
+ * Backward pass without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, result and status codes
+ * as fa_bwd, minus workspace and workspace_bytes; the call allocates nothing.
+ * The workspace lives instead in a static device array of the library, 16 MiB
+ * on every GPU the library runs on, held until the process ends: it serves
+ * B * H * N <= 2^21 query rows (for example B2 H32 N32768); larger sizes
+ * return FA_ERR_SCRATCH before any HIP call.  Every call on one GPU shares
+ * that GPU's array (the kernels write every value of it they read before
+ * reading it, so nothing carries over from the previous call), so calls
+ * that may overlap on one GPU (different streams, or another thread) race
+ * and must be serialised by the caller.  The array's device address is
+ * looked up on the first call on each device.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                   int H, int N, int D, float softmax_scale, int causal, hipStream_t stream);
 
 /*
  * Backward pass over packed variable-length sequences: the gradients of

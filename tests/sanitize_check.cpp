@@ -35,6 +35,10 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t) {
     ++g_fwd_calls;
     return hipSuccess;
 }
+hipError_t bwd_scratch(float** ptr) {  // stand-in address, never dereferenced
+    *ptr = reinterpret_cast<float*>(0x40000);
+    return hipSuccess;
+}
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t) {
     volatile int64_t sink = (int64_t)a.B + a.H + a.N + a.D + a.causal + a.f16 + a.drop.thresh +
                             a.max_seqlen;
@@ -225,6 +229,19 @@ static void abi_backward() {
     CHECK(fa_bwd_varlen(P, P, P, P, F, P, P, P, P, CU, 3, INT_MAX, 300, P, SIZE_MAX, 2, 64, 0.1f,
                         1, S) == FA_ERR_TOO_LARGE);
     CHECK(fa::g_bwd_calls == calls0 + 8);
+    const int calls1 = fa::g_bwd_calls;
+    CHECK(fa_bwd_noalloc(P, P, P, P, F, P, P, P, P, 2, 32, 32768, 128, 0.1f, 1, S) == FA_OK);
+    CHECK(fa_bwd_noalloc(P, P, P, P, F, P, P, P, P, 2, 32, 32769, 128, 0.1f, 1, S) ==
+          FA_ERR_SCRATCH);
+    CHECK(fa_bwd_noalloc(P, P, P, P, F, P, P, P, P, 65535, 65535, 8, 64, 0.1f, 1, S) ==
+          FA_ERR_SCRATCH);
+    CHECK(fa_bwd_noalloc(P, P, P, P, F, P, P, P, P, INT_MAX, 1, 8, 64, 0.1f, 1, S) ==
+          FA_ERR_SHAPE);
+    CHECK(fa_bwd_noalloc(P, P, P, P, F, P, P, P, P, 1, 1, INT_MAX, 64, 0.1f, 1, S) ==
+          FA_ERR_TOO_LARGE);
+    CHECK(fa_bwd_noalloc(P, P, P, nullptr, F, P, P, P, P, 1, 1, 8, 64, 0.1f, 1, S) ==
+          FA_ERR_NULL);
+    CHECK(fa::g_bwd_calls == calls1 + 1);
     for (int st = -3; st < 12; ++st) CHECK(fa_status_string(st) != nullptr);
 }
 

@@ -17,7 +17,7 @@ import exact_io_aware_44_amd as fa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 
-OK, NULL, SHAPE, UNSUP, ALIGN, WS, LAUNCH, ARG, TOO_LARGE = range(9)
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, LAUNCH, ARG, TOO_LARGE, SCRATCH = range(10)
 P = 0x10000          # a 16-byte-aligned stand-in address, never dereferenced
 PM = 0x10008         # misaligned by 8 bytes
 
@@ -36,6 +36,7 @@ def _declared():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert names == ["fa_bwd", "fa_bwd_dropout", "fa_bwd_dropout_f16", "fa_bwd_f16",
+                     "fa_bwd_noalloc",
                      "fa_bwd_varlen", "fa_bwd_varlen_dropout", "fa_bwd_varlen_dropout_f16",
                      "fa_bwd_varlen_f16",
                      "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_dropout",
@@ -49,7 +50,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         s = fa.fa_status_string(code)
         assert s.startswith("FA_"), s
     assert "unknown" in fa.fa_status_string(99)
@@ -189,6 +190,29 @@ def bwd(lib, q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, ws=P,
 ])
 def test_bwd_rejects(lib, kw, code):
     assert bwd(lib, **kw) == code
+
+
+def bwd_noalloc(lib, q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=2, N=64,
+                D=128, scale=0.1, causal=1):
+    return lib.fa_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, B, H, N, D, scale, causal,
+                              None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(lse=None), NULL), (dict(do=None), NULL),
+    (dict(dq=None), NULL), (dict(dk=None), NULL), (dict(dv=None), NULL),
+    (dict(B=0), SHAPE), (dict(N=0), SHAPE), (dict(H=-1), SHAPE), (dict(B=70000), SHAPE),
+    (dict(D=100), UNSUP), (dict(causal=7), UNSUP), (dict(scale=float("inf")), ARG),
+    (dict(dk=PM), ALIGN), (dict(lse=P + 4), ALIGN),
+    (dict(N=1 << 24), TOO_LARGE),
+    # the static scratch serves 2^21 query rows (B * H * N)
+    (dict(B=1, H=32, N=65537), SCRATCH), (dict(B=2, H=32, N=32769), SCRATCH),
+    (dict(B=512, H=4097, N=1), SCRATCH),
+])
+def test_bwd_noalloc_rejects(lib, kw, code):
+    """Every invalid argument is rejected before any HIP call; sizes above the
+    static scratch return FA_ERR_SCRATCH."""
+    assert bwd_noalloc(lib, **kw) == code
 
 
 def bwd_varlen(lib, q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, cu=P, nseq=2,
