@@ -16,9 +16,12 @@
 //
 // Three launches, no atomics, deterministic:
 //   1. dsum:  D_i = dO_i . O_i from the saved bf16 O (HBM-bound, tiny).
-//   2. dkdv:  one unit per 128-key tile keeps K and V in registers and streams
-//             query tiles (Q, dO, L, D) through LDS: S, P, dV += P^T dO,
-//             dP = dO V^T, dS, dK += dS^T Q.
+//   2. dkdv:  one unit per key tile keeps its keys' V (and K) on chip and
+//             streams query tiles (Q, dO, L, D) through LDS: S, P,
+//             dV += P^T dO, dP = dO V^T, dS, dK += dS^T Q.  dkdv64_kernel
+//             (64 keys per wave) runs it; the dropout replay uses
+//             dkdv_kernel (32 keys per wave), whose registers leave room
+//             for the generator.
 //   3. dq:    one unit per 128-query tile keeps Q and dO in registers and
 //             streams key tiles (K, V) through LDS: S^T, P^T, dP^T, dS^T,
 //             dQ += dS K.
@@ -511,6 +514,374 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// 2b. dK, dV with 64 keys per wave: unit = (batch, head, 256-key tile), wave
+//     w owning keys 64w .. 64w + 63.  Each Q or dO operand read from LDS
+//     (rows for S and dP, transpose reads for dV and dK) feeds two MFMAs,
+//     one per 32-key block of the wave, where dkdv_kernel's 32 keys per wave
+//     use each read once: fewer LDS instructions per MFMA, which is what
+//     bounds dkdv_kernel (its stage time is about the sum of its MFMA, LDS
+//     and VALU time).  V of the 64 keys stays in VGPRs (64), K in a padded
+//     LDS tile loaded once per key tile, and the dK^T and dV^T accumulators
+//     fill all 256 AGPRs, so a SIMD holds one wave.
+//     A 32-query block runs four phases, each operand requested PF operands
+//     ahead: S MFMAs; dP MFMAs with the weights P = exp2(S c - L log2 e)
+//     computed beside them; dV MFMAs with dS = P (dP - D) beside them; dK
+//     MFMAs.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Kv64Tile {
+    static constexpr int WK = 64;                  // keys per wave
+    static constexpr int BK = 4 * WK;              // keys per unit
+    static constexpr int BQ = 64;                  // queries per streamed stage
+    static constexpr int CPR = D / 8;              // 16-byte chunks per row
+    static constexpr int T_ELEMS = BQ * D;         // one Q or dO stage
+    static constexpr int LPW = BQ * CPR / 64 / 4;  // 1 KiB loads per wave per stage
+    static constexpr int RPL = 64 / CPR;           // rows per 1 KiB load
+    static constexpr int DS = D / 16;              // MFMA k-steps across the head width
+    static constexpr int DB = D / 32;              // 32-wide blocks of the head width
+    // K tile: row pitch padded by one 16-byte chunk, so the rows a
+    // quarter-wave reads with ds_read_b128 spread over the banks
+    static constexpr int KSTR = D + 8;
+    static constexpr int KCH = KSTR / 8;           // chunk slots per padded row
+    static constexpr int K_LOADS = WK * KCH / 64;  // 1 KiB loads per wave (own keys)
+};
+
+template <typename E, int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256, 1) void dkdv64_kernel(BwdParams p) {
+    using T = Kv64Tile<D>;
+    static_assert(T::WK * T::KCH % 64 == 0, "whole 1 KiB loads per wave");
+    // One LDS object, so every buffer is the same base plus a constant that
+    // fits a ds_read's immediate offset (separate objects would each need
+    // their own address registers).  The accesses of each stage go through
+    // __restrict__ pointers, which tells the compiler that the stage being
+    // read and the one a DMA is filling do not overlap.
+    // Layout: the two f buffers (fp32 -L log2 e, then D), the four stage
+    // buffers, then the K tile, whose reads take their base from a register
+    // (it starts past the 64 KiB an immediate offset reaches).
+    constexpr int S_OFF = 2 * (4 * T::BQ);              // two f buffers, in bf16 units
+    constexpr int K_OFF = S_OFF + 4 * T::T_ELEMS;
+    __shared__ __attribute__((aligned(16))) bf16 smem[K_OFF + T::BK * T::KSTR];
+    float* const f_lds0 = reinterpret_cast<float*>(smem);
+    float* const f_lds1 = f_lds0 + 2 * T::BQ;
+    bf16* const q_lds0 = smem + S_OFF;
+    bf16* const q_lds1 = smem + S_OFF + T::T_ELEMS;
+    bf16* const do_lds0 = smem + S_OFF + 2 * T::T_ELEMS;
+    bf16* const do_lds1 = smem + S_OFF + 3 * T::T_ELEMS;
+    bf16* const k_lds = smem + K_OFF;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int g = lane >> 4, i16 = lane & 15;
+    int head, uidx;
+    unit_of(blockIdx.x, gridDim.x, p.per_head, head, uidx);
+    int n;
+    int64_t row0;
+    slice_rows<VARLEN>(p, head, n, row0);
+    const int nkt = (n + T::BK - 1) / T::BK;
+    int kt0, kt1;
+    if (!unit_tiles(CAUSAL, false, uidx, nkt, kt0, kt1)) return;
+
+    const uint32_t bytes = (uint32_t)n * D * 2;
+    const Buf qb = make_buf(p.q + row0 * D, bytes);
+    const Buf kb = make_buf(p.k + row0 * D, bytes);
+    const Buf vb = make_buf(p.v + row0 * D, bytes);
+    const Buf dob = make_buf(p.dout + row0 * D, bytes);
+    const Buf nlb = make_buf(p.nl2 + row0, (uint32_t)n * 4);
+    const Buf ddb = make_buf(p.dd + row0, (uint32_t)n * 4);
+    const Buf dkb = make_buf(p.dk + row0 * D, bytes);
+    const Buf dvb = make_buf(p.dv + row0 * D, bytes);
+
+    // stage movement as in dkdv_kernel: wave w issues the 1 KiB loads
+    // w*LPW .. w*LPW+LPW-1 of each stage; the global chunk a lane fetches
+    // carries the swizzle
+    uint32_t qoff[T::LPW];
+#pragma unroll
+    for (int x = 0; x < T::LPW; ++x) {
+        const int L = wave * T::LPW + x;
+        const int r = L * T::RPL + lane / T::CPR;
+        const int pc = lane % T::CPR;
+        qoff[x] = (uint32_t)(r * D + ((pc ^ qd_swz<D>(r)) << 3)) * 2;
+    }
+    auto load_stage = [&](int q0, bf16* __restrict__ qd, bf16* __restrict__ dod,
+                          float* __restrict__ fd) __attribute__((always_inline)) {
+#pragma unroll
+        for (int x = 0; x < T::LPW; ++x) {
+            const int L = wave * T::LPW + x;
+            load16_lds(qb, qoff[x] + (uint32_t)q0 * D * 2, qd + 512 * L);
+            load16_lds(dob, qoff[x] + (uint32_t)q0 * D * 2, dod + 512 * L);
+        }
+        if (wave == 0) load4_lds(nlb, (uint32_t)(q0 + lane) * 4, fd);
+        if (wave == 1) load4_lds(ddb, (uint32_t)(q0 + lane) * 4, fd + T::BQ);
+    };
+
+    bf16x8 vreg[2][T::DS];               // [32-key block][k-step]
+    f32x16 dk[2][T::DB], dv[2][T::DB];      // [32-key block][32-wide d block]
+    int kw0 = 0;
+
+    // Per-lane LDS element offsets, computed once.  The swizzle depends on
+    // the row mod 16 only, so query block qb and k-step t of a transpose
+    // read add (32 qb + 16 t) * D, a constant the reads take as their
+    // immediate offset (with the buffer's place in smem) instead of each
+    // combination holding an address register.
+    int row_off[T::DS];      // Q / dO rows, k-step ss, query block 0
+#pragma unroll
+    for (int ss = 0; ss < T::DS; ++ss) row_off[ss] = qd_off<D>(l32, 2 * ss + hi);
+    int tr_off[T::DB][2];    // dO^T / Q^T, d-block e, rows +0 / +8, k-step 0
+#pragma unroll
+    for (int e = 0; e < T::DB; ++e) {
+        const int rr = 4 * hi + (i16 >> 2);
+        const int cc = 4 * e + 2 * (g & 1) + ((i16 & 3) >> 1);
+        tr_off[e][0] = qd_off<D>(rr, cc) + 4 * (i16 & 1);
+        tr_off[e][1] = qd_off<D>(rr + 8, cc) + 4 * (i16 & 1);
+    }
+    // K^T rows of key block 0, k-step 0, as an element offset from smem;
+    // hidden from the optimiser so it stays one register (block and k-step
+    // are immediates)
+    int k_off = K_OFF + (T::WK * wave + l32) * T::KSTR + 8 * hi;
+    asm volatile("" : "+v"(k_off));
+
+    // NQB (1 or 2) consecutive 32-query blocks, the first being local block
+    // qb0 of the stage (queries qg0 ..), as one stream of steps, so operand
+    // requests run ahead across the block boundary.  Step i of a block:
+    // operand i in [0, NS) Q rows (S, with the two K^T operands of the
+    // step); [NS, 2NS) dO rows (dP); [2NS, 2NS + NA) dO^T (dV); [2NS + NA,
+    // NOP) Q^T (dK); each feeds the MFMAs of both key blocks.  MASK: weights
+    // of keys after their query are zero (the wave's diagonal stage).
+    auto qrun = [&](const bf16* __restrict__ qs, const bf16* __restrict__ dos,
+                    const float* __restrict__ fs, int qb0, int qg0, auto nqb_tag,
+                    auto mask_tag) __attribute__((always_inline)) {
+        constexpr int NQB = decltype(nqb_tag)::value;
+        constexpr bool MASK = decltype(mask_tag)::value;
+        constexpr int NS = T::DS, NA = 2 * T::DB, NOP = 2 * NS + 2 * NA;
+        constexpr int NT = NQB * NOP;  // steps of the stream
+        constexpr int PF = 5;          // operand read distance, in steps (10 MFMAs)
+        auto fetch = [&](int st) -> bf16x8 {
+            const int qb = qb0 + st / NOP, i = st % NOP;
+            if (i < 2 * NS) {
+                const int ss = i % NS;
+                return lds_read16((i < NS ? qs : dos) + 32 * qb * D + row_off[ss]);
+            }
+            const int j = (i - 2 * NS) % NA;
+            const int e = j % T::DB, t = j / T::DB;
+            const bf16* src = (i < 2 * NS + NA ? dos : qs) + (32 * qb + 16 * t) * D;
+            return cat(lds_read_tr(src + tr_off[e][0]), lds_read_tr(src + tr_off[e][1]));
+        };
+        // K^T operands of an S step (rows of this wave's keys in the K tile,
+        // both key blocks), requested with the step's Q operand
+        auto kfetch = [&](int st, bf16x8 (&kk)[2]) {
+            const bf16* kr = smem + k_off + 16 * (st % NOP);
+            kk[0] = lds_read16(kr);
+            kk[1] = lds_read16(kr + 32 * T::KSTR);
+        };
+        auto is_s = [](int st) { return st % NOP < NS; };
+        f32x16 s[2], dp[2];
+        bf16x8 pb[2][2], sb[2][2];  // [key block][16-query k-step]
+        f32x4 nl{}, dd{};
+        // weights of group a (4 queries) of key block kb of stream block
+        // blk, in place in s: P = exp2(S c - L log2 e); keys after their
+        // query get zero
+        auto p_group = [&](int blk, int kb, int a) __attribute__((always_inline)) {
+            if (kb == 0)
+                nl = *reinterpret_cast<const f32x4*>(fs + 32 * (qb0 + blk) + 8 * a + 4 * hi);
+            // masked: tm > query offset in the block
+            const int tm = kw0 + 32 * kb + l32 - (qg0 + 32 * blk) - 4 * hi;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 4 * a + x;
+                float pv = exp2_fast(__builtin_fmaf(s[kb][r], p.c, nl[x]));
+                if (MASK) pv = tm > 8 * a + x ? 0.f : pv;
+                s[kb][r] = pv;
+            }
+        };
+        // dS = P (dP - D) of group a of key block kb, in place in dp
+        auto ds_group = [&](int blk, int kb, int a) __attribute__((always_inline)) {
+            if (kb == 0)
+                dd = *reinterpret_cast<const f32x4*>(fs + T::BQ + 32 * (qb0 + blk) + 8 * a +
+                                                     4 * hi);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 4 * a + x;
+                dp[kb][r] = s[kb][r] * (dp[kb][r] - dd[x]);
+            }
+        };
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 op[NT], kop[NT][2];
+#pragma unroll
+        for (int st = 0; st < PF; ++st) {
+            op[st] = fetch(st);
+            if (is_s(st)) kfetch(st, kop[st]);
+        }
+        // VALU groups spread over the dP and dV phases (8 groups each)
+#pragma clang loop unroll(full)
+        for (int st = 0; st < NT; ++st) {
+            const int i = st % NOP;
+            if (st + PF < NT) {
+                op[st + PF] = fetch(st + PF);
+                if (is_s(st + PF)) kfetch(st + PF, kop[st + PF]);
+            }
+            const int blk = st / NOP;
+            if (i == 0) s[0] = s[1] = dp[0] = dp[1] = f32x16{};  // a new block
+            if (i < NS) {
+                s[0] = mfma32<E>(op[st], kop[st][0], s[0]);
+                s[1] = mfma32<E>(op[st], kop[st][1], s[1]);
+            } else if (i < 2 * NS) {
+                const int ss = i - NS;
+                dp[0] = mfma32<E>(op[st], vreg[0][ss], dp[0]);
+                dp[1] = mfma32<E>(op[st], vreg[1][ss], dp[1]);
+                constexpr int PER = 8 / NS;  // groups per step
+#pragma unroll
+                for (int k = 0; k < PER; ++k) {
+                    const int gi = ss * PER + k;  // a-major: (a, kb)
+                    p_group(blk, gi & 1, gi >> 1);
+                }
+                if (i == 2 * NS - 1) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        pb[kb][0] = pack8<E>(s[kb], 0);
+                        pb[kb][1] = pack8<E>(s[kb], 8);
+                    }
+                }
+            } else if (i < 2 * NS + NA) {
+                // k-step t outer, d-block e inner: an accumulator recurs
+                // every 2 DB MFMAs
+                const int j = i - 2 * NS, e = j % T::DB, t = j / T::DB;
+                mfma_acc<E>(dv[0][e], op[st], pb[0][t]);
+                mfma_acc<E>(dv[1][e], op[st], pb[1][t]);
+                constexpr int PER = 8 / NA;
+#pragma unroll
+                for (int k = 0; k < PER; ++k) {
+                    const int gi = j * PER + k;
+                    ds_group(blk, gi & 1, gi >> 1);
+                }
+                if (i == 2 * NS + NA - 1) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        sb[kb][0] = pack8<E>(dp[kb], 0);
+                        sb[kb][1] = pack8<E>(dp[kb], 8);
+                    }
+                }
+            } else {
+                const int j = i - 2 * NS - NA, e = j % T::DB, t = j / T::DB;
+                mfma_acc<E>(dk[0][e], op[st], sb[0][t]);
+                mfma_acc<E>(dk[1][e], op[st], sb[1][t]);
+            }
+            // keep this order: the operand reads PF steps ahead, the step's
+            // two MFMAs, then its share of the VALU work
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    using True = std::true_type;
+    using False = std::false_type;
+
+    // One 64-query stage.  DIAG: one of the unit's first four stages, where
+    // a wave's 64 keys may follow some or all of the stage's queries (blocks
+    // wholly before the keys are skipped, the others masked: past the
+    // wave's diagonal the mask keeps every weight).
+    auto stage = [&](int qt, bool more, const bf16* __restrict__ qs,
+                     const bf16* __restrict__ dos, const float* __restrict__ fs,
+                     bf16* __restrict__ qn, bf16* __restrict__ don, float* __restrict__ fn,
+                     auto diag_tag) __attribute__((always_inline)) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
+        if (more) load_stage((qt + 1) * T::BQ, qn, don, fn);
+        const int q0 = qt * T::BQ;
+        using One = std::integral_constant<int, 1>;
+        using Two = std::integral_constant<int, 2>;
+        if (DIAG) {
+            // block by block; blocks whose queries all precede our keys are
+            // skipped
+            if (q0 + 31 >= kw0) qrun(qs, dos, fs, 0, q0, One{}, True{});
+            if (q0 + 63 >= kw0) qrun(qs, dos, fs, 1, q0 + 32, One{}, True{});
+        } else {
+            qrun(qs, dos, fs, 0, q0, Two{}, False{});
+        }
+        wait_vmem_lds();  // next stage landed; this stage's reads are done
+        barrier_only();
+    };
+
+    for (int rep = 0; rep < 2; ++rep) {
+        const int kt = rep == 0 ? kt0 : kt1;
+        if (kt < 0) break;
+        const int k0u = kt * T::BK;
+        kw0 = k0u + T::WK * wave;
+        // the lane index is hidden from the optimiser here, so the per-lane
+        // offsets of the loads below are computed per key tile instead of
+        // being hoisted out of this loop and held (spilled) across it
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int s = 0; s < T::DS; ++s) {
+                const uint32_t off =
+                    ((uint32_t)(kw0 + 32 * kb2 + (ln & 31)) * D + 16 * s + 8 * (ln >> 5)) * 2;
+                vreg[kb2][s] = __builtin_bit_cast(bf16x8, load16(vb, off));
+            }
+        // this wave's 64 K rows -> its region of the K tile (pad slots fetch
+        // nothing and write zeros); the wait and barrier below cover them
+#pragma unroll
+        for (int t = 0; t < T::K_LOADS; ++t) {
+            const int P = 64 * t + ln, r = P / T::KCH, c = P % T::KCH;
+            const uint32_t off = c < T::CPR ? ((uint32_t)(kw0 + r) * D + 8 * c) * 2 : kOutOfRange;
+            load16_lds(kb, off, k_lds + T::WK * wave * T::KSTR + 512 * t);
+        }
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int e = 0; e < T::DB; ++e) {
+                dv[kb2][e] = f32x16{};
+                dk[kb2][e] = f32x16{};
+            }
+        // under causal masking queries before the key tile see none of it
+        const int qt_begin = CAUSAL ? k0u / T::BQ : 0;
+        const int nqt = (n + T::BQ - 1) / T::BQ;
+        load_stage(qt_begin * T::BQ, q_lds0, do_lds0, f_lds0);
+        wait_vmem_lds();
+        barrier_only();
+        int qt = qt_begin;
+        if (CAUSAL) {
+            // the tile's 256 keys span its first four stages; each wave's
+            // diagonal is one of them
+            const int diag_end = min(nqt, qt_begin + T::BK / T::BQ);
+            for (; qt < diag_end; ++qt) {
+                const bool odd = (qt - qt_begin) & 1;
+                stage(qt, qt + 1 < nqt, odd ? q_lds1 : q_lds0, odd ? do_lds1 : do_lds0,
+                      odd ? f_lds1 : f_lds0, odd ? q_lds0 : q_lds1, odd ? do_lds0 : do_lds1,
+                      odd ? f_lds0 : f_lds1, True{});
+            }
+        }
+        // two stages per trip, so each reads and fills statically known LDS
+        // buffers (the parity is even here: 0 or 4 diagonal stages ran)
+        for (; qt + 1 < nqt; qt += 2) {
+            stage(qt, true, q_lds0, do_lds0, f_lds0, q_lds1, do_lds1, f_lds1, False{});
+            stage(qt + 1, qt + 2 < nqt, q_lds1, do_lds1, f_lds1, q_lds0, do_lds0, f_lds0,
+                  False{});
+        }
+        if (qt < nqt) {
+            const bool odd = (qt - qt_begin) & 1;
+            stage(qt, false, odd ? q_lds1 : q_lds0, odd ? do_lds1 : do_lds0,
+                  odd ? f_lds1 : f_lds0, odd ? q_lds0 : q_lds1, odd ? do_lds0 : do_lds1,
+                  odd ? f_lds0 : f_lds1, False{});
+        }
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int e = 0; e < T::DB; ++e) mfma_acc_drain(dv[kb2][e], dk[kb2][e]);
+        // dV[kj][d] = acc, dK[kj][d] = scale * acc, through a stage buffer of
+        // this wave's own (every wave is past the last stage's barrier)
+        static_assert(32 * (D + 8) <= T::T_ELEMS, "a wave's rows fit in one stage buffer");
+        bf16* const st = wave == 0 ? q_lds0 : wave == 1 ? q_lds1 : wave == 2 ? do_lds0 : do_lds1;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            store_rows<E, D>(st, dv[kb2], 1.f, dvb, kw0 + 32 * kb2, lane);
+            store_rows<E, D>(st, dk[kb2], p.scale, dkb, kw0 + 32 * kb2, lane);
+        }
+        // the second key tile's first stage refills these buffers
+        if (rep == 0 && kt1 >= 0) barrier_only();
+    }
+}
+
+// ---------------------------------------------------------------------------
 // 3. dQ: unit = (batch, head, 128-query tile); wave w owns queries
 //    32w..32w+31 of the tile and keeps them (Q, dO as B operands) and their
 //    dQ^T accumulator in VGPRs while 64-key stages of K and V stream through
@@ -761,11 +1132,19 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream) {
     // units per (sequence, head) come from the longest sequence; units past
     // a shorter sequence's tiles return at once
     const int nmax = VARLEN ? a.max_seqlen : a.N;
-    const int nkt = (nmax + KvTile<D>::BK - 1) / KvTile<D>::BK;
-    p.per_head = CAUSAL ? (nkt + 1) / 2 : nkt;
-    const int64_t units = (int64_t)p.per_head * a.H * a.B;
-    hipLaunchKernelGGL((dkdv_kernel<E, D, CAUSAL, DROP, VARLEN>), dim3((unsigned)units),
-                       dim3(256), 0, stream, p);
+    if constexpr (DROP) {  // the dropout replay keeps 32 keys per wave
+        const int nkt = (nmax + KvTile<D>::BK - 1) / KvTile<D>::BK;
+        p.per_head = CAUSAL ? (nkt + 1) / 2 : nkt;
+        const int64_t units = (int64_t)p.per_head * a.H * a.B;
+        hipLaunchKernelGGL((dkdv_kernel<E, D, CAUSAL, DROP, VARLEN>), dim3((unsigned)units),
+                           dim3(256), 0, stream, p);
+    } else {
+        const int nkt = (nmax + Kv64Tile<D>::BK - 1) / Kv64Tile<D>::BK;
+        p.per_head = CAUSAL ? (nkt + 1) / 2 : nkt;
+        const int64_t units = (int64_t)p.per_head * a.H * a.B;
+        hipLaunchKernelGGL((dkdv64_kernel<E, D, CAUSAL, VARLEN>), dim3((unsigned)units),
+                           dim3(256), 0, stream, p);
+    }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
 
