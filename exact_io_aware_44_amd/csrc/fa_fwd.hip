@@ -88,6 +88,7 @@ __device__ __forceinline__ int v_swz(int r) {
 // Every weight and both sums still share one reference point, so O = u / l
 // and L = m + ln l are unchanged up to rounding.
 constexpr float kLazyRescale = 8.f;
+constexpr float kLazyLimit = 256.f;  // 2^kLazyRescale
 
 struct FwdParams {
     const bf16* q;
@@ -323,6 +324,25 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         pb[1] = pack8<E>(s, 8);
         l_new = (rs[0] + rs[1]) + (rs[2] + rs[3]);  // taken against m_new
     };
+    // Interior halves (every row already has a finite running maximum, no
+    // mask, no dropout): the weights are taken against the running maximum
+    // as it stands, without first finding the half's maximum; s is left
+    // intact.  The lazy bound still holds when every weight is at most 2^8,
+    // which a row sum l_new <= 2^8 guarantees (an overflow shows there as
+    // inf); settle() checks it after the half-step and otherwise redoes the
+    // half exactly as softmax() and rescale() would, so the result is the
+    // same either way.
+    auto softmax_fast = [&](const f32x16& s, bf16x8 (&pb)[2]) {
+        float w[16], rs[4];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            w[r] = exp2_fast(__builtin_fmaf(s[r], p.c, -m_run));
+            rs[r & 3] = r < 4 ? w[r] : rs[r & 3] + w[r];
+        }
+        pb[0] = pack8<E>(w);
+        pb[1] = pack8<E>(w + 8);
+        l_new = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    };
     // Bring the old sums (u, and l before this half) to the new maximum, then
     // add this half's sum.  The log2 factor m_old - m_new is 0 on lanes whose
     // maximum did not move, and the exponential and the multiplies run only
@@ -337,6 +357,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
             l_run *= f;
         }
         l_run += l_new;
+    };
+    auto settle = [&](f32x16& s, bf16x8 (&pb)[2], int hsm) {
+        if (__any(l_new > kLazyLimit)) {  // a weight may exceed 2^8: the exact path
+            float m_use;
+            bool upd;
+            softmax(s, pb, m_use, upd, hsm, False{});
+            rescale(m_use, upd);
+        } else {
+            l_run += l_new;
+        }
     };
 
     uint32_t voffb[T::DB];
@@ -395,7 +425,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         bf16x8 op[NM > 0 ? NM : 1];
 #pragma unroll
         for (int i = 0; i < PF && i < NM; ++i) op[i] = fetch(i);
-        if constexpr (DO_SM) softmax(s_cur, pb_new, m_use, upd, hsm, chk);
+        if constexpr (DO_SM) {
+            if constexpr (!decltype(chk)::value && !DROP) softmax_fast(s_cur, pb_new);
+            else softmax(s_cur, pb_new, m_use, upd, hsm, chk);
+        }
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
             if (i + PF < NM) op[i + PF] = fetch(i + PF);
@@ -460,11 +493,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
             if (MASKED && needs_mask(2 * j + 1)) apply_mask(sB, 2 * j + 1);
             half_step(True{}, True{}, True{}, mask_tag, 2 * j + 1, k_rd, 0, v_rd, 0, sB, sA, pA,
                       pB, m_use, upd);
-            rescale(m_use, upd);
+            if (MASKED || DROP) rescale(m_use, upd);
+            else settle(sB, pB, 2 * j + 1);
             if (MASKED && needs_mask(2 * j + 2)) apply_mask(sA, 2 * j + 2);
             half_step(True{}, True{}, True{}, mask_tag, 2 * j + 2, k_rd, 1, v_rd, 1, sA, sB, pB,
                       pA, m_use, upd);
-            rescale(m_use, upd);
+            if (MASKED || DROP) rescale(m_use, upd);
+            else settle(sA, pA, 2 * j + 2);
             wait_vmem();  // K_{j+2} and V_{j+1} landed
             barrier_only();
         };
