@@ -140,7 +140,9 @@ def run_backward(torch, ai, fa, steps):
     backward = {"workload": wb.name, "ms": round(b_ms, 4),
                 "tflops": round(bflops / (b_ms * 1e-3) / 1e12, 2),
                 "frac": round(bflops / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "flops_per_call": bflops, "launches": 3}
+                "flops_per_call": bflops, "launches": 3,
+                # per call (HIP events around each call's three launches)
+                "calls": launch_stats(wb.name, bflops, bper)}
     del qb, kb, vb, dob, ob, lseb, dq, dk, dv, ws
     return backward
 
