@@ -251,6 +251,19 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     // every row precedes the first key)
     const int kend = CAUSAL ? max(0, min(nk, q0 + T::BR + shift)) : nk;
     const int nkt = (kend + T::BC - 1) / T::BC;
+    // Order of the key tiles.  The units of a head that run together on one
+    // XCD start their heavy tiles together and walk them up from key 0 in
+    // step, so they share each K/V tile in L2.  Their light tiles start at
+    // staggered times (unit u after n_tiles - u heavy steps); walked up from
+    // key 0 they would each want a different tile, but walked down from the
+    // last one, every light tile of the round reads the same key position at
+    // the same time (u's light tile has u + 1 tiles, so at time t it is at
+    // tile n_tiles - t).  Step tile t of the walk is key tile kt0(t) / BC;
+    // logical half h (the order the pipeline runs) is physical half ph(h).
+    // Any order of the key tiles gives the same softmax up to rounding.
+    const bool rev = CAUSAL && !SPLIT && tile1 >= 0 && rep == 1;
+    auto kt0 = [&](int t) { return (rev ? nkt - 1 - t : t) * T::BC; };
+    auto ph = [&](int h) { return rev ? 2 * (nkt - 1 - (h >> 1)) + (h & 1) : h; };
 
     f32x16 acc[T::DB];
 #pragma unroll
@@ -266,10 +279,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     //
     // element mask: only on halves crossing the diagonal or the sequence end;
     // element r is allowed while its key offset stays below this lane's limit
-    auto needs_mask = [&](int h) {
+    auto needs_mask = [&](int hl) {
+        const int h = ph(hl);
         return (CAUSAL && 32 * h + 31 > q0 + shift) || 32 * h + 32 > nk;
     };
-    auto apply_mask = [&](f32x16& s, int h) {
+    auto apply_mask = [&](f32x16& s, int hl) {
+        const int h = ph(hl);
         int lim = nk - 32 * h;                                  // keys before the end
         if (CAUSAL) lim = min(lim, qi + shift - 32 * h + 1);    // keys j <= qi + shift
         lim -= 4 * hi;
@@ -313,7 +328,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
             const int w = qi & 3;
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const u32x4 blk = dropout_block(p.drop, head, qi, 32 * hsm + 8 * a + 4 * hi);
+                const u32x4 blk = dropout_block(p.drop, head, qi, 32 * ph(hsm) + 8 * a + 4 * hi);
                 const uint32_t word = w == 0 ? blk[0] : w == 1 ? blk[1] : w == 2 ? blk[2] : blk[3];
 #pragma unroll
                 for (int x = 0; x < 4; ++x)
@@ -450,9 +465,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     if (nkt > 0) {
         // ---- prologue: K_0, K_1, V_0 -> LDS; S of half 0; half-step 0 (S of
         //      half 1 with the softmax of half 0) -------------------------------
-        load_k(0, k_lds0);
-        if (nkt > 1) load_k(T::BC, k_lds1);
-        load_v(0, v_lds0);
+        load_k(kt0(0), k_lds0);
+        if (nkt > 1) load_k(kt0(1), k_lds1);
+        load_v(kt0(0), v_lds0);
         wait_vmem();  // Q registers and the first tiles landed
         barrier_only();
         f32x16 sA, sB;  // scores of even / odd halves
@@ -481,15 +496,20 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         // flight while the reads proceed.
         // MASKED: the tile-step may hold halves on the causal diagonal or past
         // the end; interior tile-steps skip the checks, so their body holds
-        // no branch besides the (rare) rescale.  Interior tile-steps only run
-        // when every row of the tile reads keys 0..95 (see j_int below), so
-        // half 0 already gave each row a finite maximum: their softmax needs
-        // no -inf guard (mask_tag doubles as CHK)
+        // no branch besides the (rare) rescale.  Walking up, interior
+        // tile-steps only run when every row of the tile reads keys 0..95
+        // (see j_int below), so half 0 already gave each row a finite
+        // maximum: their softmax needs no -inf guard (mask_tag doubles as
+        // CHK).  Walking down, they follow every masked step; a row whose
+        // allowed keys all lie in interior tiles (a bottom-right mask can
+        // do that) enters them with maximum -inf, its first interior half
+        // then sums to +inf in softmax_fast(), and settle() redoes that half
+        // exactly against the half's own (finite) maximum
         auto tile_step = [&](int j, const bf16* __restrict__ k_rd, const bf16* __restrict__ v_rd,
                              bf16* __restrict__ k_wr, bf16* __restrict__ v_wr, auto mask_tag) {
             constexpr bool MASKED = decltype(mask_tag)::value;
-            if (j + 2 < nkt) load_k((j + 2) * T::BC, k_wr);
-            load_v((j + 1) * T::BC, v_wr);
+            if (j + 2 < nkt) load_k(kt0(j + 2), k_wr);
+            load_v(kt0(j + 1), v_wr);
             if (MASKED && needs_mask(2 * j + 1)) apply_mask(sB, 2 * j + 1);
             half_step(True{}, True{}, True{}, mask_tag, 2 * j + 1, k_rd, 0, v_rd, 0, sB, sA, pA,
                       pB, m_use, upd);
@@ -511,6 +531,24 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         if (CAUSAL) j_int = min(j_int, (q0 + shift - 31) / T::BC);
         j_int = max(0, min(j_int, nkt - 1));
         int j = 0;
+        if (rev) {
+            // reverse walk: masked steps first.  Physical halves from hm on
+            // need the mask; step j reads physical halves 2(nkt-1-j)+1 and
+            // 2(nkt-2-j), so it is interior once nkt-1-j <= (hm-2)/2.  The
+            // masked prefix is rounded up to an even count so the interior
+            // pairs below keep their static buffers.
+            int hm = nk / 32;
+            if (CAUSAL) hm = min(hm, q0 + shift < 31 ? 0 : (q0 + shift - 31) / 32 + 1);
+            const int tmax = hm >= 2 ? (hm - 2) / 2 : -1;
+            const int j_lo = max(0, nkt - 1 - tmax);
+            const int j_pre = min(nkt - 1, (j_lo + 1) & ~1);
+            for (; j < j_pre; ++j) {
+                const bool odd = j & 1;
+                tile_step(j, odd ? k_lds0 : k_lds1, odd ? v_lds1 : v_lds0, odd ? k_lds1 : k_lds0,
+                          odd ? v_lds0 : v_lds1, True{});
+            }
+            j_int = nkt - 1;
+        }
         // two tile-steps per trip: the buffers of each are then static
         for (; j + 1 < j_int; j += 2) {
             tile_step(j, k_lds1, v_lds0, k_lds0, v_lds1, False{});

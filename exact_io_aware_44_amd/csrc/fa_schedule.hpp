@@ -76,7 +76,8 @@ __host__ __device__ __forceinline__ bool unit_tiles(bool pairs, bool heavy_first
 }
 
 // Query tiles of a forward unit: a single tile of the split tail (rank >= 0,
-// counted from the heaviest), else the unit's pair or tile (heavy first).
+// counted from the heaviest), else the unit's pair or tile (heavy first; the
+// forward kernel walks the keys of a pair's second, light tile downwards).
 __host__ __device__ __forceinline__ bool fwd_tiles(bool pairs, int rank, int uidx, int n_tiles,
                                                    int& t0, int& t1) {
     if (rank >= 0) {

@@ -26,6 +26,9 @@ SHAPES = [  # (B, H, Nq, Nk, D): decode, short chunks, Nq > Nk, ragged tails
     (2, 2, 1, 1, 64), (2, 3, 1, 300, 128), (1, 2, 7, 129, 64), (2, 1, 128, 128, 128),
     (1, 2, 130, 70, 128), (2, 2, 200, 1000, 64), (1, 2, 64, 4100, 128),
     (1, 3, 257, 513, 128), (1, 1, 300, 37, 64),
+    # Nk - Nq = 32m + 31: the first row of a pair's light tile (whose keys
+    # the kernel walks downwards) has every allowed key in unmasked tiles
+    (1, 2, 256, 607, 128), (1, 2, 640, 1311, 64),
 ]
 
 
