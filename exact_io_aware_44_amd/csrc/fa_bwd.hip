@@ -778,12 +778,12 @@ __global__ __launch_bounds__(256, 1) void dkdv64_kernel(BwdParams p) {
     // a wave's 64 keys may follow some or all of the stage's queries (blocks
     // wholly before the keys are skipped, the others masked: past the
     // wave's diagonal the mask keeps every weight).
-    auto stage = [&](int qt, bool more, const bf16* __restrict__ qs,
+    auto stage = [&](int qt, int qt_next, const bf16* __restrict__ qs,
                      const bf16* __restrict__ dos, const float* __restrict__ fs,
                      bf16* __restrict__ qn, bf16* __restrict__ don, float* __restrict__ fn,
                      auto diag_tag) __attribute__((always_inline)) {
         constexpr bool DIAG = decltype(diag_tag)::value;
-        if (more) load_stage((qt + 1) * T::BQ, qn, don, fn);
+        if (qt_next >= 0) load_stage(qt_next * T::BQ, qn, don, fn);
         const int q0 = qt * T::BQ;
         using One = std::integral_constant<int, 1>;
         using Two = std::integral_constant<int, 2>;
@@ -835,31 +835,43 @@ __global__ __launch_bounds__(256, 1) void dkdv64_kernel(BwdParams p) {
         // under causal masking queries before the key tile see none of it
         const int qt_begin = CAUSAL ? k0u / T::BQ : 0;
         const int nqt = (n + T::BQ - 1) / T::BQ;
+        // the tile's 256 keys span its first four stages; each wave's
+        // diagonal is one of them
+        const int ndiag = CAUSAL ? min(nqt - qt_begin, T::BK / T::BQ) : 0;
+        // Walk order.  The diagonal stages come first.  The other stages of
+        // a unit's first key tile (the one with more queries) then run from
+        // the last query stage down, and those of its second tile from the
+        // diagonal up, so the units of a head that run together read the
+        // same Q/dO stage at the same time: at step i past the diagonal the
+        // first tiles are all at stage nqt - 1 - i, and a second tile (its
+        // partner's stages done) at the same stage for every pair.
+        const bool desc = CAUSAL && rep == 0;
+        auto qt_of = [&](int i) {
+            return desc && i >= ndiag ? nqt - 1 - (i - ndiag) : qt_begin + i;
+        };
+        const int ns = nqt - qt_begin;
+        auto qt_next = [&](int i) { return i + 1 < ns ? qt_of(i + 1) : -1; };
         load_stage(qt_begin * T::BQ, q_lds0, do_lds0, f_lds0);
         wait_vmem_lds();
         barrier_only();
-        int qt = qt_begin;
-        if (CAUSAL) {
-            // the tile's 256 keys span its first four stages; each wave's
-            // diagonal is one of them
-            const int diag_end = min(nqt, qt_begin + T::BK / T::BQ);
-            for (; qt < diag_end; ++qt) {
-                const bool odd = (qt - qt_begin) & 1;
-                stage(qt, qt + 1 < nqt, odd ? q_lds1 : q_lds0, odd ? do_lds1 : do_lds0,
-                      odd ? f_lds1 : f_lds0, odd ? q_lds0 : q_lds1, odd ? do_lds0 : do_lds1,
-                      odd ? f_lds0 : f_lds1, True{});
-            }
+        int i = 0;
+        for (; i < ndiag; ++i) {
+            const bool odd = i & 1;
+            stage(qt_begin + i, qt_next(i), odd ? q_lds1 : q_lds0, odd ? do_lds1 : do_lds0,
+                  odd ? f_lds1 : f_lds0, odd ? q_lds0 : q_lds1, odd ? do_lds0 : do_lds1,
+                  odd ? f_lds0 : f_lds1, True{});
         }
         // two stages per trip, so each reads and fills statically known LDS
         // buffers (the parity is even here: 0 or 4 diagonal stages ran)
-        for (; qt + 1 < nqt; qt += 2) {
-            stage(qt, true, q_lds0, do_lds0, f_lds0, q_lds1, do_lds1, f_lds1, False{});
-            stage(qt + 1, qt + 2 < nqt, q_lds1, do_lds1, f_lds1, q_lds0, do_lds0, f_lds0,
+        for (; i + 1 < ns; i += 2) {
+            stage(qt_of(i), qt_next(i), q_lds0, do_lds0, f_lds0, q_lds1, do_lds1, f_lds1,
+                  False{});
+            stage(qt_of(i + 1), qt_next(i + 1), q_lds1, do_lds1, f_lds1, q_lds0, do_lds0, f_lds0,
                   False{});
         }
-        if (qt < nqt) {
-            const bool odd = (qt - qt_begin) & 1;
-            stage(qt, false, odd ? q_lds1 : q_lds0, odd ? do_lds1 : do_lds0,
+        if (i < ns) {
+            const bool odd = i & 1;
+            stage(qt_of(i), -1, odd ? q_lds1 : q_lds0, odd ? do_lds1 : do_lds0,
                   odd ? f_lds1 : f_lds0, odd ? q_lds0 : q_lds1, odd ? do_lds0 : do_lds1,
                   odd ? f_lds0 : f_lds1, False{});
         }
