@@ -153,3 +153,13 @@ def backward_inputs(B=BACKWARD.B, H=BACKWARD.H, N=BACKWARD.N, D=BACKWARD.D,
     """q, k, v, dO bf16 [B, H, N, D] from one generator."""
     g = generator(seed)
     return tuple(randn_bf16((B, H, N, D), g) for _ in range(4))
+
+
+def randn_bf16_device(shape, seed: int):
+    """iid N(0,1) fp32 drawn on the GPU from a seeded CUDA generator, rounded
+    to bf16: for inputs of several GiB, which the CPU generator would take
+    minutes to fill.  A test copies the slices it checks back to the host, so
+    the oracle still sees exactly the bits the GPU library read."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(int(seed))
+    return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)

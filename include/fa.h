@@ -44,8 +44,10 @@
  *    rejected call has no side effect.  After validation the only error is
  *    FA_ERR_LAUNCH (the launch itself failed).  Faults inside a kernel surface
  *    at the caller's next synchronisation, as for any HIP kernel.
- *  - Per (batch, head) slice, N * D * 2 bytes must stay below 2 GiB (the
- *    kernels address one slice with 32-bit offsets); larger slices return
+ *  - Per (batch, head) slice of N rows, (N + 256) * D * 2 bytes must stay
+ *    below 2 GiB (the kernels address one slice with 32-bit offsets, and may
+ *    address up to one tile past its end; 256 rows of headroom cover that):
+ *    N <= 8388351 at D = 128, 16776959 at D = 64.  Larger slices return
  *    FA_ERR_TOO_LARGE.
  */
 #ifndef FA_MI355X_H

@@ -76,6 +76,8 @@ def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=16, D=64, scale=0.125,
     (dict(q=PM), ALIGN), (dict(k=PM), ALIGN), (dict(v=PM), ALIGN),
     (dict(o=PM), ALIGN), (dict(lse=P + 4), ALIGN),
     (dict(N=1 << 23, D=128), TOO_LARGE), (dict(N=1 << 24, D=64), TOO_LARGE),
+    # one row past the largest accepted slice: (N + 256) * D * 2 reaches 2 GiB
+    (dict(N=8388352, D=128), TOO_LARGE), (dict(N=16776960, D=64), TOO_LARGE),
 ])
 def test_fwd_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code
@@ -92,6 +94,7 @@ def fwd_qk(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=16, Nk=40, D=64, scale=0
     (dict(H=70000), SHAPE), (dict(D=80), UNSUP), (dict(causal=3), UNSUP),
     (dict(scale=float("nan")), ARG), (dict(v=PM), ALIGN), (dict(lse=P + 8), ALIGN),
     (dict(Nk=1 << 23, D=128), TOO_LARGE), (dict(Nq=1 << 24, D=64), TOO_LARGE),
+    (dict(Nk=8388352, D=128), TOO_LARGE), (dict(Nk=16776960, D=64), TOO_LARGE),
 ])
 def test_fwd_qk_rejects(lib, kw, code):
     assert fwd_qk(lib, **kw) == code
