@@ -273,9 +273,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     float l_new = 0.f;                     // sum of the latest half's weights
 
     // ---- the pipeline works on 32-key half tiles: half h holds keys
-    //      32h .. 32h+31 (LDS tile h/2, rows 32*(h%2) ..).  Its scores live in
-    //      one f32x16 (lane: query qi, keys 32h + 8(r/4) + 4hi + r%4) and its
-    //      weights in two bf16x8 B operands (k-steps of 16 keys). -------------
+    //      32h' .. 32h'+31 with h' = ph(h) (LDS tile h/2, rows 32*(h%2) ..).
+    //      Its scores live in one f32x16 (lane: query qi, keys 32h' + 8(r/4)
+    //      + 4hi + r%4) and its weights in two bf16x8 B operands (k-steps of
+    //      16 keys). -----------------------------------------------------------
     //
     // element mask: only on halves crossing the diagonal or the sequence end;
     // element r is allowed while its key offset stays below this lane's limit
