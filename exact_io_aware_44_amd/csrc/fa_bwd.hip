@@ -918,10 +918,13 @@ struct QTile {
 template <typename E, int D, bool CAUSAL, bool DROP, bool VARLEN>
 __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
     using T = QTile<D>;
-    __shared__ __attribute__((aligned(16))) bf16 k_lds0[T::T_ELEMS];
-    __shared__ __attribute__((aligned(16))) bf16 k_lds1[T::T_ELEMS];
-    __shared__ __attribute__((aligned(16))) bf16 v_lds0[T::T_ELEMS];
-    __shared__ __attribute__((aligned(16))) bf16 v_lds1[T::T_ELEMS];
+    // one LDS object, so each stage buffer is the same base plus a constant
+    // that fits a ds_read's immediate offset
+    __shared__ __attribute__((aligned(16))) bf16 smem[4 * T::T_ELEMS];
+    bf16* const k_lds0 = smem;
+    bf16* const k_lds1 = smem + T::T_ELEMS;
+    bf16* const v_lds0 = smem + 2 * T::T_ELEMS;
+    bf16* const v_lds1 = smem + 3 * T::T_ELEMS;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -965,6 +968,20 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
         }
     };
 
+    // Per-lane LDS element offsets, computed once: the swizzle depends on the
+    // row mod 16 only, so a 32-key block b and a k-step t add (32b + 16t) D,
+    // a constant the reads take as an immediate.
+    int row_off[T::DS];     // K / V rows of key block 0, k-step ss
+#pragma unroll
+    for (int ss = 0; ss < T::DS; ++ss) row_off[ss] = qd_off<D>(l32, 2 * ss + hi);
+    int tr_off[T::DB][2];   // K^T, d-block e, rows +0 / +8, key block 0, k-step 0
+#pragma unroll
+    for (int e = 0; e < T::DB; ++e) {
+        const int rr = 4 * hi + (i16 >> 2);
+        const int cc = 4 * e + 2 * (g & 1) + ((i16 & 3) >> 1);
+        tr_off[e][0] = qd_off<D>(rr, cc) + 4 * (i16 & 1);
+        tr_off[e][1] = qd_off<D>(rr + 8, cc) + 4 * (i16 & 1);
+    }
     bf16x8 qreg[T::DS], doreg[T::DS];
     f32x16 acc[T::DB];
     int qi = 0;
@@ -978,7 +995,7 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
         dp = f32x16{};
 #pragma unroll
         for (int ss = 0; ss < T::DS; ++ss) {
-            const int off = qd_off<D>(32 * b + l32, 2 * ss + hi);
+            const int off = row_off[ss] + 32 * b * D;
             s = mfma32<E>(lds_read16(ks + off), qreg[ss], s);
             dp = mfma32<E>(lds_read16(vs + off), doreg[ss], dp);
         }
@@ -1017,10 +1034,8 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
         for (int e = 0; e < T::DB; ++e)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const int rr = 32 * b + 16 * t + 4 * hi + (i16 >> 2);
-                const int cc = 4 * e + 2 * (g & 1) + ((i16 & 3) >> 1);
-                const int o0 = qd_off<D>(rr, cc) + 4 * (i16 & 1);
-                const int o1 = qd_off<D>(rr + 8, cc) + 4 * (i16 & 1);
+                const int o0 = tr_off[e][0] + (32 * b + 16 * t) * D;
+                const int o1 = tr_off[e][1] + (32 * b + 16 * t) * D;
                 acc[e] = mfma32<E>(cat(lds_read_tr(ks + o0), lds_read_tr(ks + o1)), sb[t], acc[e]);
             }
     };
@@ -1098,6 +1113,12 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
         wait_vmem_lds();
         barrier_only();
         int ks_i = 0;
+        // two plain stages per trip, so each reads and fills statically
+        // known buffers
+        for (; ks_i + 1 < n_plain; ks_i += 2) {
+            step(ks_i, true, k_lds0, v_lds0, k_lds1, v_lds1, qw0, False{});
+            step(ks_i + 1, ks_i + 2 < nks, k_lds1, v_lds1, k_lds0, v_lds0, qw0, False{});
+        }
         for (; ks_i < n_plain; ++ks_i) run_stage(ks_i, nks, qw0, False{});
         if (CAUSAL)
             for (; ks_i < nks; ++ks_i) run_stage(ks_i, nks, qw0, True{});
