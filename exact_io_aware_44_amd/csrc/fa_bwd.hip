@@ -14,17 +14,18 @@
 // (the chain rule through the softmax; the pages state only the weight
 // reconstruction and that each tile contributes to dQ, dK and dV).
 //
-// Three launches, no atomics, deterministic:
-//   1. dsum:  D_i = dO_i . O_i from the saved bf16 O (HBM-bound, tiny).
+// Two launches, no atomics, deterministic:
+//   1. dq:    one unit per 128-query tile keeps Q and dO in registers and
+//             streams key tiles (K, V) through LDS: S^T, P^T, dP^T, dS^T,
+//             dQ += dS K.  Each unit first forms D_i = dO_i . O_i from the
+//             saved bf16 O and -L_i log2 e for its rows, and also writes
+//             them to the workspace.
 //   2. dkdv:  one unit per key tile keeps its keys' V (and K) on chip and
-//             streams query tiles (Q, dO, L, D) through LDS: S, P,
+//             streams query tiles (Q, dO, -L log2 e, D) through LDS: S, P,
 //             dV += P^T dO, dP = dO V^T, dS, dK += dS^T Q.  dkdv64_kernel
 //             (64 keys per wave) runs it; the dropout replay uses
 //             dkdv_kernel (32 keys per wave), whose registers leave room
 //             for the generator.
-//   3. dq:    one unit per 128-query tile keeps Q and dO in registers and
-//             streams key tiles (K, V) through LDS: S^T, P^T, dP^T, dS^T,
-//             dQ += dS K.
 // Recomputing S and dP in the dq pass costs two extra products out of seven
 // but avoids a cross-unit reduction of dQ.
 //
@@ -126,38 +127,10 @@ __device__ __forceinline__ void store_rows(bf16* st, const f32x16* acc, float sc
 }
 
 // ---------------------------------------------------------------------------
-// 1. Per-row constants: D_i = dO_i . O_i (fp32 sum of exact bf16 products)
-//    and -L_i log2(e), the exponent offset that turns a score into its weight.
-// ---------------------------------------------------------------------------
-template <typename E, int D>
-__global__ __launch_bounds__(256) void dsum_kernel(const bf16* o, const bf16* dout,
-                                                   const float* lse, float* dd, float* nl2,
-                                                   int64_t rows) {
-    constexpr int LPR = D / 8;  // lanes per row, 16 bytes each
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t row = gid / LPR;
-    const int part = (int)(gid % LPR);
-    float acc = 0.f;
-    if (row < rows) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + row * D + part * 8);
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(dout + row * D + part * 8);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            acc = __builtin_fmaf(to_f32<E>(a[j]), to_f32<E>(b[j]), acc);
-    }
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (row < rows && part == 0) {
-        dd[row] = acc;
-        nl2[row] = -lse[row] * kLog2e;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// 2. dK, dV: unit = (batch, head, 128-key tile); wave w owns keys 32w..32w+31
-//    of the tile.  K and V (the B operands of S and dP) stay in VGPRs, the
-//    dK^T, dV^T accumulators in AGPRs, while 64-query stages of Q, dO,
-//    -L log2 e and D stream through double-buffered LDS.
+// dK, dV (dropout replay): unit = (batch, head, 128-key tile); wave w owns
+//    keys 32w..32w+31 of the tile.  K and V (the B operands of S and dP)
+//    stay in VGPRs, the dK^T, dV^T accumulators in AGPRs, while 64-query
+//    stages of Q, dO, -L log2 e and D stream through double-buffered LDS.
 // ---------------------------------------------------------------------------
 template <int D>
 struct KvTile {
@@ -894,13 +867,16 @@ __global__ __launch_bounds__(256, 1) void dkdv64_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ: unit = (batch, head, 128-query tile); wave w owns queries
+// dQ: unit = (batch, head, 128-query tile); wave w owns queries
 //    32w..32w+31 of the tile and keeps them (Q, dO as B operands) and their
 //    dQ^T accumulator in VGPRs while 64-key stages of K and V stream through
 //    double-buffered LDS.  Scores are taken transposed, S^T = K Q^T, so each
 //    lane holds one query and its L and D are scalars.  Using no AGPRs
 //    leaves the kernel the whole 256-register budget of two waves per SIMD
-//    as VGPRs (any AGPR use splits that budget in half).
+//    as VGPRs (any AGPR use splits that budget in half).  This pass runs
+//    first: each unit forms D_i = dO_i . O_i (fp32 sum of exact 16-bit
+//    products) and -L_i log2 e for its rows and also writes them to the
+//    workspace, where the dK/dV pass reads them.
 // ---------------------------------------------------------------------------
 template <int D>
 struct QTile {
@@ -949,6 +925,8 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
     const Buf nlb = make_buf(p.nl2 + row0, (uint32_t)n * 4);
     const Buf ddb = make_buf(p.dd + row0, (uint32_t)n * 4);
     const Buf dqb = make_buf(p.dq + row0 * D, bytes);
+    const Buf ob = make_buf(p.o + row0 * D, bytes);
+    const Buf lb = make_buf(p.lse + row0, (uint32_t)n * 4);
 
     uint32_t koff[T::LPW];
 #pragma unroll
@@ -1099,8 +1077,26 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
             qreg[s] = __builtin_bit_cast(bf16x8, load16(qb, off));
             doreg[s] = __builtin_bit_cast(bf16x8, load16(dob, off));
         }
-        nl2 = loadf(nlb, (uint32_t)qi * 4);
-        dd = loadf(ddb, (uint32_t)qi * 4);
+        // D_i = dO_i . O_i from the saved O (the lane pair qi, qi + 32 holds
+        // the two halves of the row) and -L_i log2 e; both also go to the
+        // workspace for the dK/dV pass, which runs after this one
+        {
+            float part = 0.f;
+#pragma unroll
+            for (int s = 0; s < T::DS; ++s) {
+                const uint32_t off = ((uint32_t)qi * D + 16 * s + 8 * hi) * 2;
+                const bf16x8 ov = __builtin_bit_cast(bf16x8, load16(ob, off));
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    part = __builtin_fmaf(to_f32<E>(ov[j]), to_f32<E>(doreg[s][j]), part);
+            }
+            dd = pair_sum(part);
+            nl2 = -loadf(lb, (uint32_t)qi * 4) * kLog2e;
+            if (hi == 0) {
+                store4(ddb, (uint32_t)qi * 4, __builtin_bit_cast(uint32_t, dd));
+                store4(nlb, (uint32_t)qi * 4, __builtin_bit_cast(uint32_t, nl2));
+            }
+        }
 #pragma unroll
         for (int e = 0; e < T::DB; ++e) acc[e] = f32x16{};
 
@@ -1156,15 +1152,18 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream) {
     p.scale = a.scale;
     p.drop = a.drop;
 
-    const int64_t threads = rows * (D / 8);
-    hipLaunchKernelGGL((dsum_kernel<E, D>), dim3((unsigned)((threads + 255) / 256)),
-                       dim3(256), 0, stream, p.o, p.dout, p.lse, p.dd, p.nl2, rows);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-
     // units per (sequence, head) come from the longest sequence; units past
     // a shorter sequence's tiles return at once
     const int nmax = VARLEN ? a.max_seqlen : a.N;
+    // the dQ pass: per_head query tiles (pairs under causal masking)
+    const int nqt = (nmax + QTile<D>::BR - 1) / QTile<D>::BR;
+    p.per_head = CAUSAL ? (nqt + 1) / 2 : nqt;
+    const int64_t qunits = (int64_t)p.per_head * a.H * a.B;
+    hipLaunchKernelGGL((dq_kernel<E, D, CAUSAL, DROP, VARLEN>), dim3((unsigned)qunits),
+                       dim3(256), 0, stream, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+
     if constexpr (DROP) {  // the dropout replay keeps 32 keys per wave
         const int nkt = (nmax + KvTile<D>::BK - 1) / KvTile<D>::BK;
         p.per_head = CAUSAL ? (nkt + 1) / 2 : nkt;
@@ -1178,15 +1177,6 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((dkdv64_kernel<E, D, CAUSAL, VARLEN>), dim3((unsigned)units),
                            dim3(256), 0, stream, p);
     }
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-
-    // the dQ pass: per_head query tiles (pairs under causal masking)
-    const int nqt = (nmax + QTile<D>::BR - 1) / QTile<D>::BR;
-    p.per_head = CAUSAL ? (nqt + 1) / 2 : nqt;
-    const int64_t qunits = (int64_t)p.per_head * a.H * a.B;
-    hipLaunchKernelGGL((dq_kernel<E, D, CAUSAL, DROP, VARLEN>), dim3((unsigned)qunits),
-                       dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
