@@ -29,3 +29,20 @@ def test_noalloc_backward_matches_fa_bwd(gpu):
         exact = oracle.bwd(q, k, v, do, ai.default_scale(D), causal)
         for name, g, r in zip(("dq", "dk", "dv"), got, exact):
             check_grad(g, r, "noalloc %s %s" % (name, (B, H, N, D)))
+
+
+def test_noalloc_at_the_scratch_limit(gpu):
+    """B2 H32 N32768 D128 causal: 2^21 query rows, the most the static array
+    serves; bit for bit against fa_bwd (inputs drawn on the GPU)."""
+    B, H, N, D = 2, 32, 32768, 128
+    assert B * H * N == 1 << 21
+    say("noalloc backward at the scratch limit", (B, H, N, D))
+    q, k, v, do = (ai.randn_bf16_device((B, H, N, D), 6300 + i) for i in range(4))
+    o, lse = gpu.fa_fwd(q, k, v, causal=True)
+    ref = gpu.fa_bwd(q, k, v, o, lse, do, causal=True)
+    got = gpu.fa_bwd_noalloc(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        assert torch.equal(g, r), name
+    del q, k, v, do, o, lse, ref, got
+    torch.cuda.empty_cache()
