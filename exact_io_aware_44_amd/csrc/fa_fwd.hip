@@ -577,7 +577,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
             half_step(False{}, True{}, False{}, True{}, 0, nullptr, 0, v_rd, 1, sA, sB, pB, pA,
                       m_use, upd);
         }
-        __syncthreads();  // LDS reads done before the next tile of the unit reloads
+        // no barrier here: the last tile-step reads only V, the epilogue
+        // below stages each wave's O rows in the K buffers (last read before
+        // the previous tile-step's barrier), and the barrier that follows the
+        // staging orders every wave's reads before the next tile's loads
     }
 
     // epilogue: O = u / l (bf16), L = m + ln l (natural log, scaled units);
