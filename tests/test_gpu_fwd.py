@@ -27,6 +27,25 @@ def test_tiny_and_stability_variant(gpu):
         check_fwd(o, lse, o_ref, l_ref, name)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_in_the_thousands(gpu, causal):
+    """Q*32 (exact in bf16): raw scores of several hundred to a thousand, so
+    the running maximum moves by far more than the lazy bound over and over
+    and the weights are nearly one-hot; every element against the oracle.
+    O is then close to single V rows, so V is halved (also exact) to keep
+    |O| below 4, where rounding O to bf16 alone stays within 2^-7."""
+    B, H, N, D = 1, 2, 777, 128
+    q, k, v = ai.qkv(B, H, N, D, seed=31)
+    q32 = (q.float() * 32).to(torch.bfloat16)
+    vh = (v.float() * 0.5).to(torch.bfloat16)
+    assert torch.equal(q32.float(), q.float() * 32) and torch.equal(vh.float(), v.float() * 0.5)
+    scale = ai.default_scale(D)
+    say("case Q*32 causal", causal)
+    o, lse = _run(gpu, q32, k, vh, scale, causal)
+    o_ref, l_ref = oracle.fwd(q32, k, vh, scale, causal)
+    check_fwd(o, lse, o_ref, l_ref, "Q*32")
+
+
 SHAPES = [  # (B, H, N, D): single rows, ragged tails, several tiles
     (1, 1, 1, 64), (1, 2, 1, 128), (2, 1, 63, 64), (1, 3, 64, 128),
     (1, 1, 127, 128), (2, 2, 129, 64), (1, 2, 200, 128), (2, 3, 300, 128),
