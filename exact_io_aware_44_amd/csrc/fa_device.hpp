@@ -68,6 +68,12 @@ __device__ __forceinline__ Buf make_buf(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 load16(Buf b, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(b.r, off, 0, 0);
 }
+// Cache-policy bit of a buffer access: nt (non-temporal), for data read or
+// written once, so it does not displace lines that other units re-read.
+constexpr int kNonTemporal = 2;
+__device__ __forceinline__ u32x4 load16_nt(Buf b, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(b.r, off, 0, kNonTemporal);
+}
 __device__ __forceinline__ void store16(Buf b, uint32_t off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, b.r, off, 0, 0);
 }

@@ -677,15 +677,16 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* part_o, const f
 //  - the four waves of a workgroup take interleaved 32-key blocks of the
 //    unit's key range (wave w: blocks w, w + 4, ...) and run independently,
 //    with no barrier until the end;
-//  - K and V blocks are read with ordinary wave-wide loads of 1 KiB of
-//    consecutive rows into registers, two blocks ahead, so each CU keeps
-//    128 KiB in flight.  (Loading the MFMA operands themselves touches 32
-//    rows per load, 32 bytes each; alone, that pattern streams at about
-//    3.8 TB/s.)  A block is then written into the wave's own LDS region,
-//    K rows padded and V rows swizzled as in fwd_kernel, and read back as
-//    MFMA operands.  (Filling the LDS by global->LDS DMA instead measured
-//    the same on this workload: about 6 TB/s is what per-head streams of
-//    this layout reach on this chip, with or without arithmetic.)
+//  - K and V blocks are read with wave-wide loads of 1 KiB of consecutive
+//    rows into registers, two blocks ahead, so each CU keeps 128 KiB in
+//    flight.  (Loading the MFMA operands themselves touches 32 rows per
+//    load, 32 bytes each; alone, that pattern streams at about 3.8 TB/s.)
+//    A block is then written into the wave's own LDS region, K rows padded
+//    and V rows swizzled as in fwd_kernel, and read back as MFMA operands.
+//    Every K/V byte is read exactly once, so the loads carry the
+//    non-temporal hint: with it the stream reaches about 6.8 TB/s on this
+//    workload, without it about 6.05 (filling the LDS by global->LDS DMA
+//    measured the same as plain loads).
 //  - at the end the waves' (m, l, u) are merged through LDS by the same
 //    running-softmax rule, then O and L (or the range's partials) are stored.
 template <int D>
@@ -782,9 +783,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(FwdParams p) {
     auto issue = [&](int i, Blk& r) {
         const uint32_t o = i < nb ? (uint32_t)phys(i) * T::BK * D * 2 + gofs : kOutOfRange;
 #pragma unroll
-        for (int t = 0; t < T::LOADS; ++t) r.k[t] = load16(kb, o + t * 1024);
+        for (int t = 0; t < T::LOADS; ++t) r.k[t] = load16_nt(kb, o + t * 1024);
 #pragma unroll
-        for (int t = 0; t < T::LOADS; ++t) r.v[t] = load16(vb, o + t * 1024);
+        for (int t = 0; t < T::LOADS; ++t) r.v[t] = load16_nt(vb, o + t * 1024);
     };
     // LDS reads of the previous block come first in the wave's LDS queue,
     // so the writes can follow them directly
