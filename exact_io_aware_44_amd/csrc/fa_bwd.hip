@@ -99,7 +99,8 @@ __device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0
 // acc[e], register r); stored directly, each store instruction would write 32
 // rows in 16-byte pieces.  The rows are staged in st (32 x (D + 8) elements,
 // this wave's own LDS region; the 16-byte row padding spreads the 8-byte
-// writes over the banks) and written back as whole rows, 16 bytes per lane.
+// writes over the banks) and written back as whole rows, 16 bytes per lane,
+// with the non-temporal hint (nothing in the pass reads them again).
 template <typename E, int D>
 __device__ __forceinline__ void store_rows(bf16* st, const f32x16* acc, float scale, Buf dst,
                                            int base, int lane) {
@@ -119,7 +120,7 @@ __device__ __forceinline__ void store_rows(bf16* st, const f32x16* acc, float sc
     for (int t = 0; t < 32 / RPI; ++t) {
         const int i = RPI * t + lane / CPR, c = lane % CPR;
         const u32x4 w = *reinterpret_cast<const u32x4*>(st + i * OSTR + 8 * c);
-        store16(dst, ((uint32_t)(base + i) * D + 8 * c) * 2, w);
+        store16_nt(dst, ((uint32_t)(base + i) * D + 8 * c) * 2, w);
     }
     // reads done before the region is written again
     __builtin_amdgcn_s_waitcnt(0xC07F);

@@ -77,6 +77,9 @@ __device__ __forceinline__ u32x4 load16_nt(Buf b, uint32_t off) {
 __device__ __forceinline__ void store16(Buf b, uint32_t off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, b.r, off, 0, 0);
 }
+__device__ __forceinline__ void store16_nt(Buf b, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, b.r, off, 0, kNonTemporal);
+}
 __device__ __forceinline__ void store8(Buf b, uint32_t off, u32x2 v) {
     __builtin_amdgcn_raw_buffer_store_b64(v, b.r, off, 0, 0);
 }

@@ -604,7 +604,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         // stored directly each store instruction would write 32 rows in
         // 16-byte pieces.  The wave stages its 32 rows in a K buffer (free
         // after the last tile-step) and writes them back as whole rows, 16
-        // bytes per lane.  Staged rows are padded by 16 bytes so the 8-byte
+        // bytes per lane, with the non-temporal hint (written once, not read
+        // again here).  Staged rows are padded by 16 bytes so the 8-byte
         // writes of 32 rows spread over the banks.
         constexpr int OSTR = D + 8;
         constexpr int RPI = 64 / T::CPR;  // rows per read-back instruction
@@ -626,7 +627,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         for (int t = 0; t < 32 / RPI; ++t) {
             const int i = RPI * t + lane / T::CPR, c = lane % T::CPR;
             const u32x4 w = *reinterpret_cast<const u32x4*>(ost + i * OSTR + 8 * c);
-            store16(ob, ((uint32_t)(q0 + 4 * i + wave) * D + 8 * c) * 2, w);
+            store16_nt(ob, ((uint32_t)(q0 + 4 * i + wave) * D + 8 * c) * 2, w);
         }
         // the next tile's loads refill the K buffers: every wave's reads first
         if (rep + 1 < ntiles) {
