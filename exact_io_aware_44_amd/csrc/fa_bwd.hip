@@ -966,19 +966,6 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
     int qi = 0;
     float nl2 = 0.f, dd = 0.f;
 
-    // S^T = K Q^T and dP^T = V dO^T for the 32-key block b of a stage; lane:
-    // query qi, local keys 32b + 8(r/4) + 4hi + r%4 (register r).
-    auto scores = [&](const bf16* __restrict__ ks, const bf16* __restrict__ vs, int b,
-                      f32x16& s, f32x16& dp) __attribute__((always_inline)) {
-        s = f32x16{};
-        dp = f32x16{};
-#pragma unroll
-        for (int ss = 0; ss < T::DS; ++ss) {
-            const int off = row_off[ss] + 32 * b * D;
-            s = mfma32<E>(lds_read16(ks + off), qreg[ss], s);
-            dp = mfma32<E>(lds_read16(vs + off), doreg[ss], dp);
-        }
-    };
     // dS^T = P^T (dP^T - D), P^T = exp2(S^T c - L log2 e), in bf16 B-operand
     // order; MASK zeroes the weights of keys after the lane's query.
     auto weights = [&](int kb0, const f32x16& s, const f32x16& dp, bf16x8* sb,
@@ -1006,17 +993,48 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
         sb[0] = pack8<E>(sf);
         sb[1] = pack8<E>(sf + 8);
     };
-    // dQ^T += K^T dS^T with K^T by transpose reads of the row-major stage.
-    auto accumulate = [&](const bf16* __restrict__ ks, int b, const bf16x8* sb)
-                          __attribute__((always_inline)) {
-#pragma unroll
-        for (int e = 0; e < T::DB; ++e)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int o0 = tr_off[e][0] + (32 * b + 16 * t) * D;
-                const int o1 = tr_off[e][1] + (32 * b + 16 * t) * D;
-                acc[e] = mfma32<E>(cat(lds_read_tr(ks + o0), lds_read_tr(ks + o1)), sb[t], acc[e]);
+    // One 32-key block b of a stage as a stream of steps in a fixed order:
+    // steps 0 .. DS-1 take S^T = K Q^T and dP^T = V dO^T one k-step at a time
+    // (lane: query qi, local keys 32b + 8(r/4) + 4hi + r%4 in register r),
+    // the weights follow the last of them, and steps DS .. take dQ^T +=
+    // K^T dS^T with K^T from transpose reads (k-step outer).  Every operand
+    // is requested PF steps ahead, and a scheduling barrier after each step
+    // keeps that distance (left to itself the compiler requested most of
+    // them one MFMA ahead).  A distance of 3 measured the same and spills.
+    auto block = [&](const bf16* __restrict__ ks, const bf16* __restrict__ vs, int b, int kb0,
+                     auto mask_tag) __attribute__((always_inline)) {
+        constexpr int NS = T::DS, NT = NS + 2 * T::DB;
+        constexpr int PF = 2;
+        bf16x8 ka[NT], va[NS];
+        auto fetch = [&](int st) __attribute__((always_inline)) {
+            if (st < NS) {
+                const int off = row_off[st] + 32 * b * D;
+                ka[st] = lds_read16(ks + off);
+                va[st] = lds_read16(vs + off);
+            } else {
+                const int j = st - NS, e = j % T::DB, t = j / T::DB;
+                const int o = (32 * b + 16 * t) * D;
+                ka[st] = cat(lds_read_tr(ks + tr_off[e][0] + o), lds_read_tr(ks + tr_off[e][1] + o));
             }
+        };
+        f32x16 s{}, dp{};
+        bf16x8 sb[2];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int st = 0; st < PF; ++st) fetch(st);
+#pragma clang loop unroll(full)
+        for (int st = 0; st < NT; ++st) {
+            if (st + PF < NT) fetch(st + PF);
+            if (st < NS) {
+                s = mfma32<E>(ka[st], qreg[st], s);
+                dp = mfma32<E>(va[st], doreg[st], dp);
+            } else {
+                const int j = st - NS, e = j % T::DB, t = j / T::DB;
+                acc[e] = mfma32<E>(ka[st], sb[t], acc[e]);
+            }
+            if (st == NS - 1) weights(kb0, s, dp, sb, mask_tag);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
     using True = std::true_type;
     using False = std::false_type;
@@ -1030,29 +1048,18 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
         constexpr bool MASKED = decltype(mask_tag)::value;
         if (more) load_stage((ks_i + 1) * T::BC, kn, vn);
         const int k0 = ks_i * T::BC;
-        f32x16 s0, dp0;
-        bf16x8 sb0[2];
         if constexpr (!MASKED) {
-            f32x16 s1, dp1;
-            bf16x8 sb1[2];
             // two workgroups per CU interleave one wave's matrix products
             // with the other's exponentials; keeping the blocks apart keeps
             // the registers within that occupancy
-            scores(ks, vs, 0, s0, dp0);
-            weights(k0, s0, dp0, sb0, False{});
-            accumulate(ks, 0, sb0);
-            __builtin_amdgcn_sched_barrier(0);
-            scores(ks, vs, 1, s1, dp1);
-            weights(k0 + 32, s1, dp1, sb1, False{});
-            accumulate(ks, 1, sb1);
+            block(ks, vs, 0, k0, False{});
+            block(ks, vs, 1, k0 + 32, False{});
         } else {
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 const int kb0 = k0 + 32 * b;
                 if (kb0 > qw0 + 31) continue;  // every key follows our queries
-                scores(ks, vs, b, s0, dp0);
-                weights(kb0, s0, dp0, sb0, True{});
-                accumulate(ks, b, sb0);
+                block(ks, vs, b, kb0, True{});
             }
         }
         wait_vmem_lds();
