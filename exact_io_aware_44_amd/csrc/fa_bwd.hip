@@ -500,7 +500,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
 //     A 32-query block runs four phases, each operand requested PF operands
 //     ahead: S MFMAs; dP MFMAs with the weights P = exp2(S c - L log2 e)
 //     computed beside them; dV MFMAs with dS = P (dP - D) beside them; dK
-//     MFMAs.
+//     MFMAs.  V is held negated and the dP accumulators start at D, so they
+//     end at D - dP and dS is one multiply (and a sign) per element.
 // ---------------------------------------------------------------------------
 template <int D>
 struct Kv64Tile {
@@ -651,7 +652,7 @@ __global__ __launch_bounds__(256, 1) void dkdv64_kernel(BwdParams p) {
         auto is_s = [](int st) { return st % NOP < NS; };
         f32x16 s[2], dp[2];
         bf16x8 pb[2][2], sb[2][2];  // [key block][16-query k-step]
-        f32x4 nl{}, dd{};
+        f32x4 nl{};
         // weights of group a (4 queries) of key block kb of stream block
         // blk, in place in s: P = exp2(S c - L log2 e); keys after their
         // query get zero
@@ -668,16 +669,29 @@ __global__ __launch_bounds__(256, 1) void dkdv64_kernel(BwdParams p) {
                 s[kb][r] = pv;
             }
         };
-        // dS = P (dP - D) of group a of key block kb, in place in dp
-        auto ds_group = [&](int blk, int kb, int a) __attribute__((always_inline)) {
-            if (kb == 0)
-                dd = *reinterpret_cast<const f32x4*>(fs + T::BQ + 32 * (qb0 + blk) + 8 * a +
-                                                     4 * hi);
+        // dS = P (dP - D) of group a of key block kb, in place in dp, which
+        // holds D - dP
+        auto ds_group = [&](int kb, int a) __attribute__((always_inline)) {
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int r = 4 * a + x;
-                dp[kb][r] = s[kb][r] * (dp[kb][r] - dd[x]);
+                dp[kb][r] = -(s[kb][r] * dp[kb][r]);
             }
+        };
+        // D of the queries of stream block blk in the accumulator layout
+        // (register 4a + x: query 8a + 4hi + x): the value both dP
+        // accumulators start from.  With V negated they accumulate D - dP,
+        // which saves the subtraction per element.
+        auto dinit = [&](int blk) __attribute__((always_inline)) {
+            f32x16 d;
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(fs + T::BQ + 32 * (qb0 + blk) +
+                                                                8 * a + 4 * hi);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) d[4 * a + x] = v[x];
+            }
+            return d;
         };
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 op[NT], kop[NT][2];
@@ -695,14 +709,20 @@ __global__ __launch_bounds__(256, 1) void dkdv64_kernel(BwdParams p) {
                 if (is_s(st + PF)) kfetch(st + PF, kop[st + PF]);
             }
             const int blk = st / NOP;
-            if (i == 0) s[0] = s[1] = dp[0] = dp[1] = f32x16{};  // a new block
+            if (i == 0) s[0] = s[1] = f32x16{};  // a new block
             if (i < NS) {
                 s[0] = mfma32<E>(op[st], kop[st][0], s[0]);
                 s[1] = mfma32<E>(op[st], kop[st][1], s[1]);
             } else if (i < 2 * NS) {
                 const int ss = i - NS;
-                dp[0] = mfma32<E>(op[st], vreg[0][ss], dp[0]);
-                dp[1] = mfma32<E>(op[st], vreg[1][ss], dp[1]);
+                if (ss == 0) {
+                    const f32x16 d = dinit(blk);
+                    dp[0] = mfma32<E>(op[st], vreg[0][ss], d);
+                    dp[1] = mfma32<E>(op[st], vreg[1][ss], d);
+                } else {
+                    dp[0] = mfma32<E>(op[st], vreg[0][ss], dp[0]);
+                    dp[1] = mfma32<E>(op[st], vreg[1][ss], dp[1]);
+                }
                 constexpr int PER = 8 / NS;  // groups per step
 #pragma unroll
                 for (int k = 0; k < PER; ++k) {
@@ -726,7 +746,7 @@ __global__ __launch_bounds__(256, 1) void dkdv64_kernel(BwdParams p) {
 #pragma unroll
                 for (int k = 0; k < PER; ++k) {
                     const int gi = j * PER + k;
-                    ds_group(blk, gi & 1, gi >> 1);
+                    ds_group(gi & 1, gi >> 1);
                 }
                 if (i == 2 * NS + NA - 1) {
 #pragma unroll
@@ -789,7 +809,10 @@ __global__ __launch_bounds__(256, 1) void dkdv64_kernel(BwdParams p) {
             for (int s = 0; s < T::DS; ++s) {
                 const uint32_t off =
                     ((uint32_t)(kw0 + 32 * kb2 + (ln & 31)) * D + 16 * s + 8 * (ln >> 5)) * 2;
-                vreg[kb2][s] = __builtin_bit_cast(bf16x8, load16(vb, off));
+                // negated (sign bit of each 16-bit element): see dinit
+                vreg[kb2][s] = __builtin_bit_cast(
+                    bf16x8, load16(vb, off) ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u,
+                                                    0x80008000u});
             }
         // this wave's 64 K rows -> its region of the K tile (pad slots fetch
         // nothing and write zeros); the wait and barrier below cover them
