@@ -8,7 +8,8 @@ the forward kernel, the backward pass (fa_bwd, B2 H32 N4096 D128 causal)
 against the same roofline, the decoding-shaped forward (fa_fwd_splitkv, one
 query against a 16384-token cache, B8 H32 D128) against HBM bandwidth, the
 varlen (16 packed causal sequences) and long-context (B1 H32 N65536)
-forwards, the varlen backward (fa_bwd_varlen), the metric workload with
+forwards, the varlen backward (fa_bwd_varlen), chunked prefill (fa_fwd_qk),
+the fp16 forward, dropout forward and backward, the metric workload with
 L2/MALL flushed before each launch, and
 the fp64 CPU oracle timed on a bounded sample of the same workload.
 
@@ -241,6 +242,73 @@ def run_other_configs(torch, ai, fa, steps):
     return out
 
 
+def run_next_rows(torch, ai, fa, steps):
+    """The widened entry points on shapes of their own, same roofline:
+    chunked prefill (fa_fwd_qk: 4096 new queries against a 16384-key cache,
+    causal mask aligned bottom-right), the fp16 twin of the metric forward,
+    and attention dropout (p = 0.1) forward and backward on the backward's
+    shape.  Dropout's flops are counted as without it (the generator's work
+    is not counted)."""
+    out = {}
+    B, H, Nq, Nk, D = 1, 32, 4096, 16384, 128
+    log("chunked prefill: B%d H%d Nq%d Nk%d D%d" % (B, H, Nq, Nk, D))
+    q = gpu_randn_bf16(torch, (B, H, Nq, D), 7000)
+    k, v = (gpu_randn_bf16(torch, (B, H, Nk, D), 7001 + i) for i in range(2))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+    scale = ai.default_scale(D)
+
+    def qkstep():
+        fa.fa_fwd_qk(q, k, v, softmax_scale=scale, causal=True, out=o, lse=lse)
+
+    _, per = time_launches(torch, qkstep, steps, 10)
+    pairs = Nq * (Nk - Nq) + Nq * (Nq + 1) / 2  # query i reads keys 0 .. i + Nk - Nq
+    out["chunked_prefill"] = launch_stats(
+        "chunked prefill B1 H32 Nq4096 Nk16384 D128 causal (fa_fwd_qk)", 4.0 * D * B * H * pairs,
+        per)
+    del q, k, v, o, lse
+    w = ai.CAUSAL
+    log("fp16:", w.name)
+    q, k, v = (gpu_randn_bf16(torch, (w.B, w.H, w.N, w.D), w.seed * 10 + 5 + i).to(torch.float16)
+               for i in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+
+    def hstep():
+        fa.fa_fwd(q, k, v, softmax_scale=w.scale, causal=True, out=o, lse=lse)
+
+    _, per = time_launches(torch, hstep, steps, 10)
+    out["fp16_forward"] = launch_stats(w.name + " fp16", fwd_flops(w.B, w.H, w.N, w.D, True), per)
+    del q, k, v, o, lse
+    wb = ai.BACKWARD
+    log("dropout p=0.1:", wb.name)
+    q, k, v, do = (gpu_randn_bf16(torch, (wb.B, wb.H, wb.N, wb.D), wb.seed * 10 + 5 + i)
+                   for i in range(4))
+    o = torch.empty_like(q)
+    lse = torch.empty((wb.B, wb.H, wb.N), dtype=torch.float32, device="cuda")
+    drop = dict(dropout_p=0.1, seed=1234, offset=0)
+
+    def dfstep():
+        fa.fa_fwd(q, k, v, softmax_scale=wb.scale, causal=True, out=o, lse=lse, **drop)
+
+    _, per = time_launches(torch, dfstep, steps, 10)
+    fflops = fwd_flops(wb.B, wb.H, wb.N, wb.D, True)
+    out["dropout_forward"] = launch_stats(wb.name.replace("bwd", "fwd") + " dropout 0.1", fflops,
+                                          per)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa.fa_bwd_workspace_size(wb.B, wb.H, wb.N, wb.D), dtype=torch.uint8,
+                     device="cuda")
+
+    def dbstep():
+        fa.fa_bwd(q, k, v, o, lse, do, softmax_scale=wb.scale, causal=True, dq=dq, dk=dk,
+                  dv=dv, workspace=ws, **drop)
+
+    _, per = time_launches(torch, dbstep, steps, 5)
+    out["dropout_backward"] = launch_stats(wb.name + " dropout 0.1", 2.5 * fflops, per)
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    return out
+
+
 def launch_stats(name, flops, per):
     """Per-launch median / min / mean of HIP-event durations (ms) and the
     TFLOP/s of the median against the bf16 peak."""
@@ -279,8 +347,8 @@ def main(argv=None):
     ap.add_argument("--bwd-steps", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--config-steps", type=int, default=10,
-                    help="launches of the varlen and long workloads and of the "
-                         "flushed-cache run (0 = skip)")
+                    help="launches of the varlen, long, chunked-prefill, fp16 and "
+                         "dropout workloads and of the flushed-cache run (0 = skip)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -333,6 +401,7 @@ def main(argv=None):
     decode = None
     if args.decode_steps > 0:
         decode = run_decode(torch, ai, fa, args.decode_steps)
+    nexts = run_next_rows(torch, ai, fa, args.config_steps) if args.config_steps > 0 else {}
     others = run_other_configs(torch, ai, fa, args.config_steps) if args.config_steps > 0 else {}
     torch.cuda.synchronize()
     before_s = time.perf_counter() - t_other
@@ -384,6 +453,10 @@ def main(argv=None):
         "varlen": others.get("varlen"),
         "varlen_backward": others.get("varlen_backward"),
         "long": others.get("long"),
+        "chunked_prefill": nexts.get("chunked_prefill"),
+        "fp16_forward": nexts.get("fp16_forward"),
+        "dropout_forward": nexts.get("dropout_forward"),
+        "dropout_backward": nexts.get("dropout_backward"),
     }
     if rank == 0 and args.cpu_budget > 0:
         log("cpu baseline (oracle), about %.0f s" % args.cpu_budget)
