@@ -261,19 +261,39 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     // P = exp2(S c - L log2 e) and dS = P (dP - D), rounded to bf16 in the
     // B-operand order of the two 16-query k-steps; MASK zeroes the weights
     // of keys after their query (tiles on the causal diagonal only).
+    // Dropout decisions of one 32-query block for this lane's key: word a
+    // holds group a (queries qb0 + 8a + 4hi + x in byte x).  A generator
+    // call covers 4 queries x 4 keys, so the four lanes of a quad (keys
+    // j0 .. j0+3) need the same four calls, one per group: lane t makes the
+    // call of group t, and the quad trades bytes (v_perm_b32 gathers byte c
+    // of the four words, a DPP move reads the partner's), one call per lane
+    // instead of four.
+    auto drop_words = [&](int qb0) __attribute__((always_inline)) {
+        const int t = kj & 3;
+        const u32x4 mine = dropout_block(p.drop, head, qb0 + 8 * t + 4 * hi, kj);
+        auto bytes = [&](int c) {  // byte x = byte c of mine[x]
+            const uint32_t sel = (uint32_t)c | ((uint32_t)(4 + c) << 8) | 0x0C0C0000u;
+            const uint32_t lo = __builtin_amdgcn_perm(mine[1], mine[0], sel);
+            const uint32_t up = __builtin_amdgcn_perm(mine[3], mine[2], sel);
+            return __builtin_amdgcn_perm(up, lo, 0x05040100u);
+        };
+        // got[d]: group t ^ d, from quad lane t ^ d (quad_perm xor 1, 2, 3)
+        const uint32_t got0 = bytes(t);
+        const uint32_t got1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)bytes(t ^ 1), 0xB1, 0xF, 0xF, false);
+        const uint32_t got2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)bytes(t ^ 2), 0x4E, 0xF, 0xF, false);
+        const uint32_t got3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)bytes(t ^ 3), 0x1B, 0xF, 0xF, false);
+        auto got = [&](int d) { return d == 0 ? got0 : d == 1 ? got1 : d == 2 ? got2 : got3; };
+        return u32x4{got(t), got(t ^ 1), got(t ^ 2), got(t ^ 3)};
+    };
     auto weights_group = [&](const float* __restrict__ fs, int qb0, int b, const f32x16& s,
-                             const f32x16& dp, float* pf, float* sf, int a, auto mask_tag)
-                             __attribute__((always_inline)) {
+                             const f32x16& dp, float* pf, float* sf, int a, const u32x4& dw,
+                             auto mask_tag) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int tm = kj - qb0 - 4 * hi;  // masked where tm > local query offset
         {
             const f32x4 nl = *reinterpret_cast<const f32x4*>(fs + 32 * b + 8 * a + 4 * hi);
             const f32x4 dd =
                 *reinterpret_cast<const f32x4*>(fs + T::BQ + 32 * b + 8 * a + 4 * hi);
-            // dropout: one generator call covers this lane's key and the 4
-            // queries of group a (word x: query +x; byte: key % 4)
-            u32x4 blk{};
-            if constexpr (DROP) blk = dropout_block(p.drop, head, qb0 + 8 * a + 4 * hi, kj);
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int r = 4 * a + x;
@@ -281,7 +301,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
                 if (MASK) pv = tm > 8 * a + x ? 0.f : pv;
                 if constexpr (DROP) {
                     // dV takes the kept weights P Z, dS = P (dP Z - D)
-                    const float z = dropout_keep(blk[x], kj & 3, p.drop.thresh)
+                    const float z = dropout_keep(a == 0 ? dw[0] : a == 1 ? dw[1] : a == 2 ? dw[2] : dw[3],
+                                                 x, p.drop.thresh)
                                         ? p.drop.inv_keep : 0.f;
                     pf[r] = pv * z;
                     sf[r] = pv * (dp[r] * z - dd[x]);
@@ -296,8 +317,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
                        const f32x16& dp, bf16x8* pb, bf16x8* sb, auto mask_tag)
                        __attribute__((always_inline)) {
         float pf[16], sf[16];
+        u32x4 dw{};
+        if constexpr (DROP) dw = drop_words(qb0);
 #pragma unroll
-        for (int a = 0; a < 4; ++a) weights_group(fs, qb0, b, s, dp, pf, sf, a, mask_tag);
+        for (int a = 0; a < 4; ++a) weights_group(fs, qb0, b, s, dp, pf, sf, a, dw, mask_tag);
         pb[0] = pack8<E>(pf);
         pb[1] = pack8<E>(pf + 8);
         sb[0] = pack8<E>(sf);
@@ -381,6 +404,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
                            lds_read_tr(src + qd_off<D>(rr + 8, cc) + 4 * (i16 & 1)));
             };
             float pf1[16], sf1[16];
+            u32x4 dw1{};
+            if constexpr (DROP) dw1 = drop_words(q0 + 32);
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 const bf16x8* pb = b ? pb1 : pb0;
@@ -398,7 +423,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
                     // evenly over block 0's MFMAs
                     constexpr int GAP = NAC / 4;
                     if (b == 0 && j % GAP == GAP - 1)
-                        weights_group(fs, q0 + 32, 1, s1, dp1, pf1, sf1, j / GAP, False{});
+                        weights_group(fs, q0 + 32, 1, s1, dp1, pf1, sf1, j / GAP, dw1, False{});
                 }
                 if (b == 0) {
                     pb1[0] = pack8<E>(pf1);
@@ -916,7 +941,7 @@ struct QTile {
 };
 
 template <typename E, int D, bool CAUSAL, bool DROP, bool VARLEN>
-__global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     using T = QTile<D>;
     // one LDS object, so each stage buffer is the same base plus a constant
     // that fits a ds_read's immediate offset
@@ -996,18 +1021,31 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void dq_kernel(BwdParams p) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int lim = qi - kb0 - 4 * hi;  // masked where local key offset > lim
         float sf[16];
-        u32x4 blk{};
+        // Dropout: a generator call covers 4 queries x 4 keys and this lane
+        // needs word qi % 4 of the calls for its 4 key groups (keys kb0 + 8g
+        // + 4hi ..).  The four lanes of a quad (queries q .. q+3) need the
+        // same four calls, so lane t makes the call of group t and the quad
+        // trades words with DPP moves: wd[g] is word qi % 4 of group g.
+        uint32_t wd[4] = {};
+        if constexpr (DROP) {
+            const int t = qi & 3;
+            const u32x4 mine = dropout_block(p.drop, head, qi, kb0 + 8 * t + 4 * hi);
+            auto word = [&](int w) { return w == 0 ? mine[0] : w == 1 ? mine[1] : w == 2 ? mine[2] : mine[3]; };
+            // got[d]: word t of group t ^ d, from quad lane t ^ d
+            const uint32_t got0 = word(t);
+            const uint32_t got1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)word(t ^ 1), 0xB1, 0xF, 0xF, false);
+            const uint32_t got2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)word(t ^ 2), 0x4E, 0xF, 0xF, false);
+            const uint32_t got3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)word(t ^ 3), 0x1B, 0xF, 0xF, false);
+            auto got = [&](int d) { return d == 0 ? got0 : d == 1 ? got1 : d == 2 ? got2 : got3; };
+#pragma unroll
+            for (int g = 0; g < 4; ++g) wd[g] = got(g ^ t);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float pv = exp2_fast(__builtin_fmaf(s[r], p.c, nl2));
             if (MASK) pv = 8 * (r >> 2) + (r & 3) > lim ? 0.f : pv;
             if constexpr (DROP) {
-                // one generator call per group of 4 keys; this lane reads the
-                // word of its query
-                if ((r & 3) == 0) blk = dropout_block(p.drop, head, qi, kb0 + 8 * (r >> 2) + 4 * hi);
-                const int w = qi & 3;
-                const uint32_t word = w == 0 ? blk[0] : w == 1 ? blk[1] : w == 2 ? blk[2] : blk[3];
-                const float z = dropout_keep(word, r & 3, p.drop.thresh) ? p.drop.inv_keep : 0.f;
+                const float z = dropout_keep(wd[r >> 2], r & 3, p.drop.thresh) ? p.drop.inv_keep : 0.f;
                 sf[r] = pv * (dp[r] * z - dd);
             } else {
                 sf[r] = pv * (dp[r] - dd);
