@@ -262,28 +262,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     // B-operand order of the two 16-query k-steps; MASK zeroes the weights
     // of keys after their query (tiles on the causal diagonal only).
     // Dropout decisions of one 32-query block for this lane's key: word a
-    // holds group a (queries qb0 + 8a + 4hi + x in byte x).  A generator
-    // call covers 4 queries x 4 keys, so the four lanes of a quad (keys
-    // j0 .. j0+3) need the same four calls, one per group: lane t makes the
-    // call of group t, and the quad trades bytes (v_perm_b32 gathers byte c
-    // of the four words, a DPP move reads the partner's), one call per lane
-    // instead of four.
+    // holds group a (queries qb0 + 8a + 4hi + x in byte x).  The four lanes
+    // of a quad (keys j0 .. j0+3) need the same four generator calls, one per
+    // group: lane t makes the call of group t and the quad trades columns.
     auto drop_words = [&](int qb0) __attribute__((always_inline)) {
         const int t = kj & 3;
         const u32x4 mine = dropout_block(p.drop, head, qb0 + 8 * t + 4 * hi, kj);
-        auto bytes = [&](int c) {  // byte x = byte c of mine[x]
-            const uint32_t sel = (uint32_t)c | ((uint32_t)(4 + c) << 8) | 0x0C0C0000u;
-            const uint32_t lo = __builtin_amdgcn_perm(mine[1], mine[0], sel);
-            const uint32_t up = __builtin_amdgcn_perm(mine[3], mine[2], sel);
-            return __builtin_amdgcn_perm(up, lo, 0x05040100u);
-        };
-        // got[d]: group t ^ d, from quad lane t ^ d (quad_perm xor 1, 2, 3)
-        const uint32_t got0 = bytes(t);
-        const uint32_t got1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)bytes(t ^ 1), 0xB1, 0xF, 0xF, false);
-        const uint32_t got2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)bytes(t ^ 2), 0x4E, 0xF, 0xF, false);
-        const uint32_t got3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)bytes(t ^ 3), 0x1B, 0xF, 0xF, false);
-        auto got = [&](int d) { return d == 0 ? got0 : d == 1 ? got1 : d == 2 ? got2 : got3; };
-        return u32x4{got(t), got(t ^ 1), got(t ^ 2), got(t ^ 3)};
+        return quad_share(t, [&](int c) { return block_column(mine, c); });
     };
     auto weights_group = [&](const float* __restrict__ fs, int qb0, int b, const f32x16& s,
                              const f32x16& dp, float* pf, float* sf, int a, const u32x4& dw,
@@ -301,8 +286,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
                 if (MASK) pv = tm > 8 * a + x ? 0.f : pv;
                 if constexpr (DROP) {
                     // dV takes the kept weights P Z, dS = P (dP Z - D)
-                    const float z = dropout_keep(a == 0 ? dw[0] : a == 1 ? dw[1] : a == 2 ? dw[2] : dw[3],
-                                                 x, p.drop.thresh)
+                    const float z = dropout_keep(dw[a], x, p.drop.thresh)
                                         ? p.drop.inv_keep : 0.f;
                     pf[r] = pv * z;
                     sf[r] = pv * (dp[r] * z - dd[x]);
@@ -1024,21 +1008,13 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
         // Dropout: a generator call covers 4 queries x 4 keys and this lane
         // needs word qi % 4 of the calls for its 4 key groups (keys kb0 + 8g
         // + 4hi ..).  The four lanes of a quad (queries q .. q+3) need the
-        // same four calls, so lane t makes the call of group t and the quad
-        // trades words with DPP moves: wd[g] is word qi % 4 of group g.
-        uint32_t wd[4] = {};
+        // same four calls: lane t makes the call of group t and the quad
+        // trades words, wd[g] being word qi % 4 of group g.
+        u32x4 wd{};
         if constexpr (DROP) {
             const int t = qi & 3;
             const u32x4 mine = dropout_block(p.drop, head, qi, kb0 + 8 * t + 4 * hi);
-            auto word = [&](int w) { return w == 0 ? mine[0] : w == 1 ? mine[1] : w == 2 ? mine[2] : mine[3]; };
-            // got[d]: word t of group t ^ d, from quad lane t ^ d
-            const uint32_t got0 = word(t);
-            const uint32_t got1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)word(t ^ 1), 0xB1, 0xF, 0xF, false);
-            const uint32_t got2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)word(t ^ 2), 0x4E, 0xF, 0xF, false);
-            const uint32_t got3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)word(t ^ 3), 0x1B, 0xF, 0xF, false);
-            auto got = [&](int d) { return d == 0 ? got0 : d == 1 ? got1 : d == 2 ? got2 : got3; };
-#pragma unroll
-            for (int g = 0; g < 4; ++g) wd[g] = got(g ^ t);
+            wd = quad_share(t, [&](int c) { return block_word(mine, c); });
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {

@@ -239,4 +239,35 @@ __device__ __forceinline__ bool dropout_keep(uint32_t word, int byte, uint32_t t
     return ((word >> (8 * byte)) & 0xFFu) >= thresh;
 }
 
+// Sharing generator calls inside a quad of lanes (lanes 4m .. 4m+3, t = lane
+// % 4).  Where the quad's lanes hold the 4 queries (or the 4 keys) of one
+// block and each needs the same 4 blocks, lane t computes block t and the
+// quad trades the pieces: part(c) is the 32-bit piece of this lane's block
+// that quad lane c needs; the result's element g is the piece of block g
+// meant for this lane.  DPP quad permutations xor 1, 2 and 3 (quad_perm
+// selectors 0xB1, 0x4E, 0x1B) read the partners' registers; every lane of
+// the quad must be active.
+template <typename F>
+__device__ __forceinline__ u32x4 quad_share(int t, F part) {
+    // g_d = what quad lane t ^ d computed for this lane: a piece of block t ^ d
+    const uint32_t g0 = part(t);
+    const uint32_t g1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)part(t ^ 1), 0xB1, 0xF, 0xF, false);
+    const uint32_t g2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)part(t ^ 2), 0x4E, 0xF, 0xF, false);
+    const uint32_t g3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)part(t ^ 3), 0x1B, 0xF, 0xF, false);
+    auto got = [&](int d) { return d == 0 ? g0 : d == 1 ? g1 : d == 2 ? g2 : g3; };
+    return u32x4{got(t), got(t ^ 1), got(t ^ 2), got(t ^ 3)};
+}
+// word w of a block (w run-time)
+__device__ __forceinline__ uint32_t block_word(const u32x4& b, int w) {
+    return w == 0 ? b[0] : w == 1 ? b[1] : w == 2 ? b[2] : b[3];
+}
+// byte c of each of a block's 4 words, packed (byte x from word x)
+__device__ __forceinline__ uint32_t block_column(const u32x4& b, int c) {
+    // v_perm_b32: selector bytes 0-3 take the second source, 4-7 the first
+    const uint32_t sel = (uint32_t)c | ((uint32_t)(4 + c) << 8) | 0x0C0C0000u;
+    const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], sel);
+    const uint32_t up = __builtin_amdgcn_perm(b[3], b[2], sel);
+    return __builtin_amdgcn_perm(up, lo, 0x05040100u);
+}
+
 }  // namespace fa

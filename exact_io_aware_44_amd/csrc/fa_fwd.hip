@@ -238,7 +238,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 
     for (int rep = 0; rep < ntiles; ++rep) {
     const int q0 = (rep == 0 ? tile0 : tile1) * T::BR;
-    const int qi = q0 + 4 * l32 + wave;  // query row held by this lane
+    // Query row held by this lane: the waves interleave (every fourth row),
+    // so each wave meets the causal diagonal's mask in the same measure.
+    // Under dropout a wave holds 32 consecutive rows instead, which puts the
+    // 4 queries of one generator call in one quad of lanes.
+    auto row_of = [&](int l) { return DROP ? q0 + 32 * wave + l : q0 + 4 * l + wave; };
+    const int qi = row_of(l32);
 
     // Q as the B operand of S^T = K Q^T: lane holds Q[qi][16s + 8hi + 0..7].
     bf16x8 qreg[T::DS];
@@ -324,17 +329,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         }
         if constexpr (DROP) {
             // dropped weights leave the P.V operand, not the sum l (L is the
-            // log-sum-exp of all allowed scores); each group of 4 keys is one
-            // generator call, this lane reading the word of its query
-            const int w = qi & 3;
+            // log-sum-exp of all allowed scores).  Each group a of 4 keys is
+            // one generator call and this lane reads the word of its query;
+            // the quad's lanes (queries q .. q+3) need the same 4 calls, so
+            // lane t makes the call of group t and the quad trades words.
+            const int t = qi & 3;
+            const u32x4 mine = dropout_block(p.drop, head, qi, 32 * ph(hsm) + 8 * t + 4 * hi);
+            const u32x4 wd = quad_share(t, [&](int c) { return block_word(mine, c); });
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const u32x4 blk = dropout_block(p.drop, head, qi, 32 * ph(hsm) + 8 * a + 4 * hi);
-                const uint32_t word = w == 0 ? blk[0] : w == 1 ? blk[1] : w == 2 ? blk[2] : blk[3];
+            for (int a = 0; a < 4; ++a)
 #pragma unroll
                 for (int x = 0; x < 4; ++x)
-                    if (!dropout_keep(word, x, p.drop.thresh)) s[4 * a + x] = 0.f;
-            }
+                    if (!dropout_keep(wd[a], x, p.drop.thresh)) s[4 * a + x] = 0.f;
         }
         pb[0] = pack8<E>(s, 0);
         pb[1] = pack8<E>(s, 8);
@@ -627,7 +633,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         for (int t = 0; t < 32 / RPI; ++t) {
             const int i = RPI * t + lane / T::CPR, c = lane % T::CPR;
             const u32x4 w = *reinterpret_cast<const u32x4*>(ost + i * OSTR + 8 * c);
-            store16_nt(ob, ((uint32_t)(q0 + 4 * i + wave) * D + 8 * c) * 2, w);
+            store16_nt(ob, ((uint32_t)row_of(i) * D + 8 * c) * 2, w);
         }
         // the next tile's loads refill the K buffers: every wave's reads first
         if (rep + 1 < ntiles) {
