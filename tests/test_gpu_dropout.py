@@ -29,13 +29,13 @@ def _codes_from_mask(keep, D):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("p,seed,offset", [(0.25, 1, 0), (0.5, 123456789012345, 7),
-                                           (0.1, 5, 4000000000)])
-def test_forward_mask_is_exact(gpu, causal, p, seed, offset):
+@pytest.mark.parametrize("p,seed,offset,D", [(0.25, 1, 0, 128), (0.5, 123456789012345, 7, 128),
+                                             (0.1, 5, 4000000000, 128), (0.3, 77, 3, 64)])
+def test_forward_mask_is_exact(gpu, causal, p, seed, offset, D):
     """q = 0 makes every weight 1/n_i; with v the code basis, O_i spells out
     row i's decisions, which must equal the oracle's bit for bit."""
-    B, H, N, D = 1, 3, 512, 128
-    say("dropout fwd mask", p, seed, offset, causal)
+    B, H, N = 1, 3, 4 * D
+    say("dropout fwd mask", p, seed, offset, causal, D)
     q = torch.zeros(B, H, N, D, dtype=torch.bfloat16)
     k = ai.randn_bf16((B, H, N, D), 2000)
     v = _code_basis(N, D).expand(B, H, N, D).contiguous()
@@ -54,11 +54,13 @@ def test_forward_mask_is_exact(gpu, causal, p, seed, offset):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_backward_replays_the_mask_exactly(gpu, causal):
+@pytest.mark.parametrize("D", [128, 64])
+def test_backward_replays_the_mask_exactly(gpu, causal, D):
     """q = 0 again; dO the code basis: dV_j = sum_i P_ij Z_ij dO_i spells out
     column j of the mask as the dK/dV pass replays it."""
-    B, H, N, D = 1, 2, 512, 128
+    B, H, N = 1, 2, 4 * D
     p, seed, offset = 0.3, 99, 12
+    say("dropout bwd mask", causal, D)
     q = torch.zeros(B, H, N, D, dtype=torch.bfloat16).cuda()
     k = ai.randn_bf16((B, H, N, D), 2100).cuda()
     v = ai.randn_bf16((B, H, N, D), 2101).cuda()
