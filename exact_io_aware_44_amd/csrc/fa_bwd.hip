@@ -268,7 +268,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     auto drop_words = [&](int qb0) __attribute__((always_inline)) {
         const int t = kj & 3;
         const u32x4 mine = dropout_block(p.drop, head, qb0 + 8 * t + 4 * hi, kj);
-        return quad_share(t, [&](int c) { return block_column(mine, c); });
+        // column t ^ d of this lane's call goes to quad lane t ^ d
+        return quad_share(t, u32x4{block_column(mine, t), block_column(mine, t ^ 1),
+                                   block_column(mine, t ^ 2), block_column(mine, t ^ 3)});
     };
     auto weights_group = [&](const float* __restrict__ fs, int qb0, int b, const f32x16& s,
                              const f32x16& dp, float* pf, float* sf, int a, const u32x4& dw,
@@ -1014,7 +1016,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
         if constexpr (DROP) {
             const int t = qi & 3;
             const u32x4 mine = dropout_block(p.drop, head, qi, kb0 + 8 * t + 4 * hi);
-            wd = quad_share(t, [&](int c) { return block_word(mine, c); });
+            wd = quad_share(t, xor_permute(mine, t));  // word t ^ d to quad lane t ^ d
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {

@@ -239,27 +239,29 @@ __device__ __forceinline__ bool dropout_keep(uint32_t word, int byte, uint32_t t
     return ((word >> (8 * byte)) & 0xFFu) >= thresh;
 }
 
+// The 4 words of v in the order of an XOR with t (0..3): element g is
+// v[g ^ t].  Two rounds of selects, no branches.
+__device__ __forceinline__ u32x4 xor_permute(const u32x4& v, int t) {
+    const bool s1 = (t & 1) != 0, s2 = (t & 2) != 0;
+    const u32x4 a{s1 ? v[1] : v[0], s1 ? v[0] : v[1], s1 ? v[3] : v[2], s1 ? v[2] : v[3]};
+    return u32x4{s2 ? a[2] : a[0], s2 ? a[3] : a[1], s2 ? a[0] : a[2], s2 ? a[1] : a[3]};
+}
+
 // Sharing generator calls inside a quad of lanes (lanes 4m .. 4m+3, t = lane
 // % 4).  Where the quad's lanes hold the 4 queries (or the 4 keys) of one
 // block and each needs the same 4 blocks, lane t computes block t and the
-// quad trades the pieces: part(c) is the 32-bit piece of this lane's block
-// that quad lane c needs; the result's element g is the piece of block g
-// meant for this lane.  DPP quad permutations xor 1, 2 and 3 (quad_perm
-// selectors 0xB1, 0x4E, 0x1B) read the partners' registers; every lane of
-// the quad must be active.
-template <typename F>
-__device__ __forceinline__ u32x4 quad_share(int t, F part) {
-    // g_d = what quad lane t ^ d computed for this lane: a piece of block t ^ d
-    const uint32_t g0 = part(t);
-    const uint32_t g1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)part(t ^ 1), 0xB1, 0xF, 0xF, false);
-    const uint32_t g2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)part(t ^ 2), 0x4E, 0xF, 0xF, false);
-    const uint32_t g3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)part(t ^ 3), 0x1B, 0xF, 0xF, false);
-    auto got = [&](int d) { return d == 0 ? g0 : d == 1 ? g1 : d == 2 ? g2 : g3; };
-    return u32x4{got(t), got(t ^ 1), got(t ^ 2), got(t ^ 3)};
-}
-// word w of a block (w run-time)
-__device__ __forceinline__ uint32_t block_word(const u32x4& b, int w) {
-    return w == 0 ? b[0] : w == 1 ? b[1] : w == 2 ? b[2] : b[3];
+// quad trades the pieces: p[d] is the 32-bit piece of this lane's block that
+// quad lane t ^ d needs; the result's element g is the piece of block g meant
+// for this lane.  DPP quad permutations xor 1, 2 and 3 (quad_perm selectors
+// 0xB1, 0x4E, 0x1B) read the partners' registers; every lane of the quad
+// must be active.
+__device__ __forceinline__ u32x4 quad_share(int t, const u32x4& p) {
+    // element d: what quad lane t ^ d computed for this lane, a piece of
+    // block t ^ d
+    const u32x4 got{p[0], (uint32_t)__builtin_amdgcn_mov_dpp((int)p[1], 0xB1, 0xF, 0xF, false),
+                    (uint32_t)__builtin_amdgcn_mov_dpp((int)p[2], 0x4E, 0xF, 0xF, false),
+                    (uint32_t)__builtin_amdgcn_mov_dpp((int)p[3], 0x1B, 0xF, 0xF, false)};
+    return xor_permute(got, t);
 }
 // byte c of each of a block's 4 words, packed (byte x from word x)
 __device__ __forceinline__ uint32_t block_column(const u32x4& b, int c) {

@@ -335,7 +335,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
             // lane t makes the call of group t and the quad trades words.
             const int t = qi & 3;
             const u32x4 mine = dropout_block(p.drop, head, qi, 32 * ph(hsm) + 8 * t + 4 * hi);
-            const u32x4 wd = quad_share(t, [&](int c) { return block_word(mine, c); });
+            // word t ^ d of this lane's call goes to quad lane t ^ d
+            const u32x4 wd = quad_share(t, xor_permute(mine, t));
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
