@@ -1,5 +1,5 @@
 """GPU parity on seeded random shapes: every entry point against the fp64
-oracle on sizes drawn from three fixed seeds (odd lengths, ragged tiles,
+oracle on sizes drawn from fixed seeds (odd lengths, ragged tiles,
 single rows, empty varlen sequences, more queries than keys), so that cases
 between the hand-picked ones are covered too."""
 import numpy as np
@@ -39,6 +39,22 @@ def _cases(seed):
     return dense, qk, varlen
 
 
+def _dropout_cases(seed):
+    """Dropout cases from a generator of their own: (B, H, N, D, causal, p,
+    seed, offset) dense and (lengths, H, D, causal, p, seed, offset) packed,
+    with 64-bit seeds and offsets anywhere in [0, 2^32)."""
+    rng = np.random.default_rng(seed)
+    dense = [(int(rng.integers(1, 3)), int(rng.integers(1, 3)), int(rng.integers(1, 600)),
+              int(rng.choice([64, 128])), bool(rng.integers(0, 2)),
+              round(float(rng.uniform(0.05, 0.6)), 3), int(rng.integers(0, 2**63)),
+              int(rng.integers(0, 2**32))) for _ in range(12)]
+    packed = [([int(x) for x in rng.integers(0, 300, size=int(rng.integers(1, 6)))],
+               int(rng.integers(1, 3)), int(rng.choice([64, 128])), bool(rng.integers(0, 2)),
+               round(float(rng.uniform(0.05, 0.6)), 3), int(rng.integers(0, 2**63)),
+               int(rng.integers(0, 2**32))) for _ in range(4)]
+    return dense, packed
+
+
 DENSE, QK, VARLEN, DENSE_BWD = [], [], [], []
 for _seed in (20260, 777, 4242):
     _d, _q, _v = _cases(_seed)
@@ -46,6 +62,7 @@ for _seed in (20260, 777, 4242):
     QK += _q
     VARLEN += _v
     DENSE_BWD += _d[:8]
+DROP_DENSE, DROP_PACKED = _dropout_cases(9090)
 
 
 @pytest.mark.parametrize("case", DENSE, ids=lambda c: "B%dH%dN%dD%dc%d" % c)
@@ -113,3 +130,48 @@ def test_varlen(gpu, case):
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.fwd_varlen(q, k, v, cu, scale, causal)
     check_fwd(o, lse, o_ref, l_ref, str(case))
+
+
+@pytest.mark.parametrize("case", DROP_DENSE, ids=lambda c: "B%dH%dN%dD%dc%d_p%s" % c[:6])
+def test_dropout_forward_backward(gpu, case):
+    B, H, N, D, causal, p, seed, offset = case
+    say("case", case)
+    q, k, v = ai.qkv(B, H, N, D, 7000 + N)
+    do = ai.randn_bf16((B, H, N, D), 7100 + N)
+    scale = ai.default_scale(D)
+    qc, kc, vc, doc = (x.cuda() for x in (q, k, v, do))
+    kw = dict(softmax_scale=scale, causal=causal, dropout_p=p, seed=seed, offset=offset)
+    o, lse = gpu.fa_fwd(qc, kc, vc, **kw)
+    grads = gpu.fa_bwd(qc, kc, vc, o, lse, doc, **kw)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.fwd_dropout(q, k, v, scale, causal, p, seed, offset)
+    check_fwd(o, lse, o_ref, l_ref, str(case))
+    refs = oracle.bwd_dropout(q, k, v, do, scale, causal, p, seed, offset)
+    for name, g, r in zip(("dQ", "dK", "dV"), grads, refs):
+        say("  %s rel-L2 whole %.3e, worst 64-row block %.3e"
+            % (name, *check_grad(g, r, "%s %s" % (case, name))))
+
+
+@pytest.mark.parametrize("case", DROP_PACKED,
+                         ids=lambda c: "n%dH%dD%dc%d_p%s" % (len(c[0]), c[1], c[2], c[3], c[4]))
+def test_dropout_packed_forward_backward(gpu, case):
+    lengths, H, D, causal, p, seed, offset = case
+    say("case", case)
+    if sum(lengths) == 0:
+        lengths = lengths[:-1] + [1]
+    cu = ai.cu_seqlens(lengths)
+    total = int(cu[-1])
+    g = ai.generator(7200 + total)
+    q, k, v, do = (ai.randn_bf16((H, total, D), g) for _ in range(4))
+    scale = ai.default_scale(D)
+    qc, kc, vc, doc, cuc = (x.cuda() for x in (q, k, v, do, cu))
+    kw = dict(softmax_scale=scale, causal=causal, dropout_p=p, seed=seed, offset=offset)
+    o, lse = gpu.fa_fwd_varlen(qc, kc, vc, cuc, max(lengths), **kw)
+    grads = gpu.fa_bwd_varlen(qc, kc, vc, o, lse, doc, cuc, max(lengths), **kw)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.fwd_varlen_dropout(q, k, v, cu, scale, causal, p, seed, offset)
+    check_fwd(o.cpu(), lse.cpu(), o_ref, l_ref, str(case))
+    refs = oracle.bwd_varlen_dropout(q, k, v, do, cu, scale, causal, p, seed, offset)
+    for name, got, want in zip(("dQ", "dK", "dV"), grads, refs):
+        say("  %s rel-L2 whole %.3e, worst 64-row block %.3e"
+            % (name, *check_grad(got.cpu(), want, "%s %s" % (case, name), cu=cu)))
