@@ -474,9 +474,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
         // two interior stages per trip, so each reads and fills statically
         // known LDS buffers and its operand addresses are a per-lane offset
         // plus a constant (the stage parity is even here: 0 or 2 diagonal
-        // stages ran); the dropout kernel keeps one stage per trip, which
-        // fits its registers
-        if (!DROP && ((qt - qt_begin) & 1) == 0) {
+        // stages ran)
+        if (((qt - qt_begin) & 1) == 0) {
             for (; qt + 1 < nqt; qt += 2) {
                 step(qt, true, q_lds0, do_lds0, f_lds0, q_lds1, do_lds1, f_lds1, False{});
                 step(qt + 1, qt + 2 < nqt, q_lds1, do_lds1, f_lds1, q_lds0, do_lds0, f_lds0,
