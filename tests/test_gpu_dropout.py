@@ -30,7 +30,8 @@ def _codes_from_mask(keep, D):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("p,seed,offset,D", [(0.25, 1, 0, 128), (0.5, 123456789012345, 7, 128),
-                                             (0.1, 5, 4000000000, 128), (0.3, 77, 3, 64)])
+                                             (0.1, 5, 4000000000, 128), (0.3, 77, 3, 64),
+                                             (0.995, 2**64 - 1, 2**32 - 1, 128)])
 def test_forward_mask_is_exact(gpu, causal, p, seed, offset, D):
     """q = 0 makes every weight 1/n_i; with v the code basis, O_i spells out
     row i's decisions, which must equal the oracle's bit for bit."""
