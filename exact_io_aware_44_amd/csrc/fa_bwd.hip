@@ -258,9 +258,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
             dp = mfma32<E>(lds_read16(dos + off), vreg[ss], dp);
         }
     };
-    // P = exp2(S c - L log2 e) and dS = P (dP - D), rounded to bf16 in the
-    // B-operand order of the two 16-query k-steps; MASK zeroes the weights
-    // of keys after their query (tiles on the causal diagonal only).
     // Dropout decisions of one 32-query block for this lane's key: word a
     // holds group a (queries qb0 + 8a + 4hi + x in byte x).  The four lanes
     // of a quad (keys j0 .. j0+3) need the same four generator calls, one per
@@ -272,6 +269,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
         return quad_share(t, u32x4{block_column(mine, t), block_column(mine, t ^ 1),
                                    block_column(mine, t ^ 2), block_column(mine, t ^ 3)});
     };
+    // P = exp2(S c - L log2 e) and dS = P (dP - D), rounded to bf16 in the
+    // B-operand order of the two 16-query k-steps; MASK zeroes the weights
+    // of keys after their query (tiles on the causal diagonal only).  Under
+    // dropout dw holds the block's decisions as drop_words returns them.
     auto weights_group = [&](const float* __restrict__ fs, int qb0, int b, const f32x16& s,
                              const f32x16& dp, float* pf, float* sf, int a, const u32x4& dw,
                              auto mask_tag) __attribute__((always_inline)) {
