@@ -7,7 +7,7 @@ import torch
 
 import attn_inputs as ai
 import oracle
-from _parity import check_fwd, check_grad, f64, say
+from _parity import check_fwd, check_grad, dropout_scale, f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -114,7 +114,7 @@ def test_forward_backward_full_oracle(gpu, shape, causal):
                             dropout_p=p, seed=seed, offset=offset)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.fwd_dropout(q, k, v, scale, causal, p, seed, offset)
-    check_fwd(o, lse, o_ref, l_ref, "dropout " + str(shape))
+    check_fwd(o, lse, o_ref, l_ref, "dropout " + str(shape), scale=dropout_scale(p))
     ref = oracle.bwd_dropout(q, k, v, do, scale, causal, p, seed, offset)
     for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         say("  %s rel-L2 whole %.3e, worst 64-row block %.3e"
@@ -126,7 +126,7 @@ def test_f16_and_zero_probability(gpu):
     o, lse = gpu.fa_fwd(q, k, v, causal=True, dropout_p=0.4, seed=3, offset=1)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.fwd_dropout(q, k, v, ai.default_scale(128), True, 0.4, 3, 1)
-    check_fwd(o, lse, o_ref, l_ref, "f16 dropout")
+    check_fwd(o, lse, o_ref, l_ref, "f16 dropout", scale=dropout_scale(0.4))
     # a probability below 1/512 rounds to T = 0: plain attention, bit for bit
     a = gpu.fa_fwd(q, k, v, causal=True, dropout_p=1e-3, seed=3, offset=1)
     b = gpu.fa_fwd(q, k, v, causal=True)

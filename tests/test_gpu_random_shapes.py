@@ -8,7 +8,7 @@ import torch
 
 import attn_inputs as ai
 import oracle
-from _parity import check_fwd, check_grad, f64, say
+from _parity import check_fwd, check_grad, dropout_scale, f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -145,7 +145,7 @@ def test_dropout_forward_backward(gpu, case):
     grads = gpu.fa_bwd(qc, kc, vc, o, lse, doc, **kw)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.fwd_dropout(q, k, v, scale, causal, p, seed, offset)
-    check_fwd(o, lse, o_ref, l_ref, str(case))
+    check_fwd(o, lse, o_ref, l_ref, str(case), scale=dropout_scale(p))
     refs = oracle.bwd_dropout(q, k, v, do, scale, causal, p, seed, offset)
     for name, g, r in zip(("dQ", "dK", "dV"), grads, refs):
         say("  %s rel-L2 whole %.3e, worst 64-row block %.3e"
@@ -170,7 +170,7 @@ def test_dropout_packed_forward_backward(gpu, case):
     grads = gpu.fa_bwd_varlen(qc, kc, vc, o, lse, doc, cuc, max(lengths), **kw)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.fwd_varlen_dropout(q, k, v, cu, scale, causal, p, seed, offset)
-    check_fwd(o.cpu(), lse.cpu(), o_ref, l_ref, str(case))
+    check_fwd(o.cpu(), lse.cpu(), o_ref, l_ref, str(case), scale=dropout_scale(p))
     refs = oracle.bwd_varlen_dropout(q, k, v, do, cu, scale, causal, p, seed, offset)
     for name, got, want in zip(("dQ", "dK", "dV"), grads, refs):
         say("  %s rel-L2 whole %.3e, worst 64-row block %.3e"

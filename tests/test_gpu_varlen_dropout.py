@@ -7,7 +7,7 @@ import torch
 
 import attn_inputs as ai
 import oracle
-from _parity import check_fwd, check_grad, f64, say
+from _parity import check_fwd, check_grad, dropout_scale, f64, say
 from test_gpu_dropout import _code_basis, _codes_from_mask
 
 pytestmark = pytest.mark.gpu
@@ -65,7 +65,8 @@ def test_packed_forward_backward_full_oracle(gpu, causal, D):
                               causal=causal, dropout_p=p, seed=seed, offset=offset)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.fwd_varlen_dropout(q, k, v, cu, scale, causal, p, seed, offset)
-    check_fwd(o.cpu(), lse.cpu(), o_ref, l_ref, "packed dropout %s" % lengths)
+    check_fwd(o.cpu(), lse.cpu(), o_ref, l_ref, "packed dropout %s" % lengths,
+              scale=dropout_scale(p))
     refs = oracle.bwd_varlen_dropout(q, k, v, do, cu, scale, causal, p, seed, offset)
     for name, got, want in zip(("dQ", "dK", "dV"), grads, refs):
         say("  %s rel-L2 whole %.3e, worst 64-row block %.3e"
@@ -88,7 +89,7 @@ def test_packed_fp16_dropout(gpu):
     torch.cuda.synchronize()
     assert o.dtype == torch.float16
     o_ref, l_ref = oracle.fwd_varlen_dropout(q, k, v, cu, scale, True, p, seed, offset)
-    check_fwd(o.cpu(), lse.cpu(), o_ref, l_ref, "packed fp16 dropout")
+    check_fwd(o.cpu(), lse.cpu(), o_ref, l_ref, "packed fp16 dropout", scale=dropout_scale(p))
     refs = oracle.bwd_varlen_dropout(q, k, v, do, cu, scale, True, p, seed, offset)
     for name, got, want in zip(("dQ", "dK", "dV"), grads, refs):
         check_grad(got.cpu(), want, "packed fp16 dropout " + name, cu=cu)
